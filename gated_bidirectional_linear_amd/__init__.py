@@ -1,0 +1,154 @@
+"""Gated bidirectional ReLU linear attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libgla.so`` (declared in
+``include/gla.h``).  It only checks tensors and marshals device pointers and
+the current HIP stream; every step of the operator runs in the HIP kernels.
+PyTorch provides device memory and streams.
+
+    out = forward(q, k, v, beta, g, rms_w, (T, H, W), eps=1e-6)
+    out = block_causal_forward(q, k, v, beta, g, rms_w, (T, H, W), state_S, state_z,
+                               block_frames, eps=1e-6)
+
+q, k, v, g: [N, heads, d] (float32 or bfloat16, contiguous, on the GPU),
+beta: [N, heads] same dtype, rms_w: [d] float32, N = T*H*W, d in {32, 64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import LIB_PATH, LibraryNotBuilt, SIGNATURES, load
+
+__all__ = [
+    "forward",
+    "block_causal_forward",
+    "status_string",
+    "version",
+    "GlaError",
+    "LibraryNotBuilt",
+    "LIB_PATH",
+    "SIGNATURES",
+    "timing_enable",
+    "timing_read",
+    "DTYPE_F32",
+    "DTYPE_BF16",
+]
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+NUM_KERNELS = 4
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def status_string(status: int) -> str:
+    return load().gla_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().gla_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check(name, t, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _common(q, k, v, beta, g, rms_w, grid, out):
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [N, heads, d]")
+    T, H, W = (int(x) for x in grid)
+    N, heads, d = (int(x) for x in q.shape)
+    if N != T * H * W:
+        raise ValueError(f"q has {N} tokens but the grid {T}x{H}x{W} has {T * H * W}")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    dt = q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("g", g, q.shape), ("beta", beta, (N, heads)),
+                         ("q", q, q.shape)):
+        _check(name, t, shp, dt, q.device)
+    _check("rms_w", rms_w, (d,), torch.float32, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check("out", out, q.shape, dt, q.device)
+    return T, H, W, heads, d, code, out
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else ctypes.c_void_p(0)
+
+
+def forward(q, k, v, beta, g, rms_w, grid, eps: float = 1e-6, out=None, stream=None):
+    """Bidirectional operator; returns ``out`` (allocated if not given)."""
+    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    st = load().gla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W, heads, d,
+                            float(eps), _ptr(out), _stream_handle(stream, q.device), code)
+    if st != 0:
+        raise GlaError(st, "gla_forward")
+    return out
+
+
+def block_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, block_frames: int,
+                         eps: float = 1e-6, out=None, stream=None):
+    """Block-causal operator.  ``state_S`` [heads, d, d] and ``state_z`` [heads, d]
+    (float32) are read as the carried state and overwritten in place with the
+    state after the last block.  Returns ``out``."""
+    torch = _torch()
+    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    _check("state_S", state_S, (heads, d, d), torch.float32, q.device)
+    _check("state_z", state_z, (heads, d), torch.float32, q.device)
+    st = load().gla_block_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
+                                         heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
+                                         _ptr(state_S), _ptr(state_z), int(block_frames), code)
+    if st != 0:
+        raise GlaError(st, "gla_block_causal_forward")
+    return out
+
+
+def timing_enable(on: bool = True) -> None:
+    st = load().gla_timing_enable(1 if on else 0)
+    if st != 0:
+        raise GlaError(st, "gla_timing_enable")
+
+
+def timing_read() -> dict:
+    """Per-kernel (milliseconds, launches) accumulated since the last read."""
+    lib = load()
+    ms = (ctypes.c_double * NUM_KERNELS)()
+    n = (ctypes.c_longlong * NUM_KERNELS)()
+    st = lib.gla_timing_read(ms, n, NUM_KERNELS)
+    if st != 0:
+        raise GlaError(st, "gla_timing_read")
+    return {lib.gla_kernel_name(i).decode(): (ms[i], int(n[i])) for i in range(NUM_KERNELS)}

@@ -1,0 +1,291 @@
+// C ABI of the operator: argument validation, token partition, stream-ordered
+// scratch, launch sequencing and optional per-kernel event timing.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+#include "../../include/gla.h"
+#include "gla_launch.h"
+
+namespace {
+
+using gla::Geometry;
+
+constexpr int kTile = 64;
+// Workgroups aimed for per launch: pass 1 writes one partial state per
+// workgroup, so it stays near two per CU (256 CUs); pass 2 has no such cost
+// and takes more for load balance.  Overridable for tuning sweeps.
+constexpr int kDefaultTargetWg1 = 512;
+constexpr int kDefaultTargetWg2 = 2048;
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (s == nullptr || *s == 0) return dflt;
+  const long v = std::strtol(s, nullptr, 10);
+  return (v >= 1 && v <= (1 << 24)) ? (int)v : dflt;
+}
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames) {
+  Geometry G{};
+  G.T = T; G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
+  G.N = T * H * W;
+  const int frames = (block_frames > 0 && block_frames < T) ? block_frames : T;
+  G.seg_len = frames * H * W;
+  G.nseg = ceil_div(G.N, G.seg_len);
+  const int tiles_per_seg = ceil_div(G.seg_len, kTile);
+  const int per_seg_heads = heads * G.nseg;
+
+  const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", kDefaultTargetWg1), per_seg_heads);
+  int cps1 = want1 < 1 ? 1 : want1;
+  if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
+  if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
+  G.chunk1 = ceil_div(tiles_per_seg, cps1) * kTile;
+  G.cps1 = ceil_div(G.seg_len, G.chunk1);
+
+  const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", kDefaultTargetWg2), per_seg_heads);
+  int cps2 = want2 < 1 ? 1 : want2;
+  if (cps2 > tiles_per_seg) cps2 = tiles_per_seg;
+  G.chunk2 = ceil_div(tiles_per_seg, cps2) * kTile;
+  G.cps2 = ceil_div(G.seg_len, G.chunk2);
+  return G;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// timing instrumentation
+// ---------------------------------------------------------------------------
+struct EventTimer final : gla::Timer {
+  struct Rec { int id; hipEvent_t a, b; };
+  bool on = false;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> open;   // per kernel id, start event awaiting its end
+  std::mutex mu;
+  EventTimer() : open(gla::kNumKernels, nullptr) {}
+  void begin(int id, hipStream_t s) override {
+    if (!on) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, s);
+    open[id] = e;
+  }
+  void end(int id, hipStream_t s) override {
+    if (!on || open[id] == nullptr) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, s);
+    recs.push_back({id, open[id], e});
+    open[id] = nullptr;
+  }
+};
+
+EventTimer& timer() {
+  static EventTimer t;
+  return t;
+}
+
+struct NullTimer final : gla::Timer {
+  void begin(int, hipStream_t) override {}
+  void end(int, hipStream_t) override {}
+};
+
+// ---------------------------------------------------------------------------
+// memory pool: keep freed scratch cached in the pool between calls
+// ---------------------------------------------------------------------------
+std::mutex g_pool_mu;
+bool g_pool_ready[256] = {false};
+
+void prepare_pool() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (g_pool_ready[dev]) return;
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    uint64_t thr = UINT64_MAX;
+    hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+  }
+  g_pool_ready[dev] = true;
+}
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+struct Range { uintptr_t lo, hi; };
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + bytes};
+}
+
+int validate(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
+             int T, int H, int W, int heads, int d, float eps, const void* out, int dtype, bool causal,
+             const float* S, const float* z, int block_frames) {
+  if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16) return GLA_ERR_DTYPE;
+  if (d != 32 && d != 64 && d != 128) return GLA_ERR_UNSUPPORTED_D;
+  if (T < 0 || H < 0 || W < 0 || heads < 1) return GLA_ERR_SHAPE;
+  if (!(std::isfinite(eps) && eps > 0.0f)) return GLA_ERR_SHAPE;
+  if (causal && block_frames < 1) return GLA_ERR_SHAPE;
+  const long long N = (long long)T * H * W;
+  if (N >= (1LL << 31)) return GLA_ERR_SHAPE;
+  if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
+  if (heads > (1 << 20)) return GLA_ERR_SHAPE;
+  if (N == 0) return GLA_OK;  // nothing is read or written
+  const void* ptrs[] = {q, k, v, beta, g, rms_w, out, causal ? S : rms_w, causal ? z : rms_w};
+  for (const void* p : ptrs)
+    if (p == nullptr) return GLA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GLA_ERR_ALIGN;
+  const size_t es = dtype == GLA_DTYPE_BF16 ? 2 : 4;
+  const size_t big = (size_t)N * heads * d * es;
+  const Range rin[] = {range_of(q, big), range_of(k, big), range_of(v, big), range_of(g, big),
+                       range_of(beta, (size_t)N * heads * es), range_of(rms_w, (size_t)d * 4)};
+  const Range rout = range_of(out, big);
+  for (const Range& r : rin)
+    if (overlap(rout, r)) return GLA_ERR_ALIAS;
+  if (causal) {
+    const Range rs = range_of(S, (size_t)heads * d * d * 4);
+    const Range rz = range_of(z, (size_t)heads * d * 4);
+    if (overlap(rs, rz) || overlap(rs, rout) || overlap(rz, rout)) return GLA_ERR_ALIAS;
+    for (const Range& r : rin)
+      if (overlap(rs, r) || overlap(rz, r)) return GLA_ERR_ALIAS;
+  }
+  return GLA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w, int T,
+        int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S, float* z,
+        int block_frames) {
+  const bool causal = S != nullptr || z != nullptr || block_frames > 0;
+  const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z, block_frames);
+  if (st != GLA_OK) return st;
+  const long long N = (long long)T * H * W;
+  if (N == 0) return GLA_OK;
+
+  const Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0);
+  const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
+  const size_t sz = (size_t)d * d + d;
+  const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
+  const size_t state_bytes = align256((size_t)G.nseg * heads * sz * 4);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  prepare_pool();
+  void* scratch = nullptr;
+  if (hipMallocAsync(&scratch, rope_bytes + part_bytes + state_bytes, hs) != hipSuccess || scratch == nullptr) {
+    (void)hipGetLastError();
+    return GLA_ERR_ALLOC;
+  }
+  char* base = static_cast<char*>(scratch);
+
+  gla::LaunchArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g; a.rms_w = rms_w; a.out = out;
+  a.S_in = S; a.z_in = z; a.S_out = S; a.z_out = z;
+  a.rope = reinterpret_cast<float2*>(base);
+  a.partial = reinterpret_cast<float*>(base + rope_bytes);
+  a.states = reinterpret_cast<float*>(base + rope_bytes + part_bytes);
+  a.bf16 = dtype == GLA_DTYPE_BF16;
+  a.stream = hs;
+  a.geo = G;
+
+  hipError_t e;
+  EventTimer& tm = timer();
+  if (tm.on) {
+    std::lock_guard<std::mutex> lk(tm.mu);
+    e = gla::launch_operator(a, tm);
+  } else {
+    NullTimer nt;
+    e = gla::launch_operator(a, nt);
+  }
+  const hipError_t ef = hipFreeAsync(scratch, hs);
+  if (e != hipSuccess || ef != hipSuccess) {
+    (void)hipGetLastError();
+    return GLA_ERR_HIP;
+  }
+  return GLA_OK;
+}
+
+const char* const kKernelNames[gla::kNumKernels] = {"rope_table_kernel", "state_partial_kernel",
+                                                     "state_reduce_kernel", "output_kernel"};
+
+}  // namespace
+
+extern "C" {
+
+int gla_forward(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
+                int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype) {
+  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr, nullptr, 0);
+}
+
+int gla_block_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                             const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                             void* stream, float* state_S, float* state_z, int block_frames, int dtype) {
+  if (block_frames < 1) {
+    // validate the rest first so dtype/d errors keep their precedence
+    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
+    return st != GLA_OK ? st : GLA_ERR_SHAPE;
+  }
+  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S, state_z, block_frames);
+}
+
+const char* gla_status_string(int status) {
+  switch (status) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL: return "a required pointer is NULL";
+    case GLA_ERR_SHAPE: return "invalid shape, block size, eps or size overflow";
+    case GLA_ERR_DTYPE: return "unknown dtype";
+    case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case GLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case GLA_ERR_ALLOC: return "temporary device memory could not be obtained";
+    case GLA_ERR_UNSUPPORTED_D: return "head dim must be 32, 64 or 128";
+    case GLA_ERR_ALIAS: return "output or state buffer overlaps another tensor";
+    default: return "unknown status";
+  }
+}
+
+int gla_version(void) { return (1 << 16) | 0; }
+
+int gla_timing_enable(int on) {
+  EventTimer& tm = timer();
+  std::lock_guard<std::mutex> lk(tm.mu);
+  tm.on = on != 0;
+  return GLA_OK;
+}
+
+int gla_timing_read(double* ms, long long* launches, int n) {
+  EventTimer& tm = timer();
+  std::lock_guard<std::mutex> lk(tm.mu);
+  int st = GLA_OK;
+  for (int i = 0; i < n && i < gla::kNumKernels; ++i) {
+    if (ms) ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (auto& r : tm.recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) st = GLA_ERR_HIP;
+    if (r.id < n) {
+      if (ms) ms[r.id] += t;
+      if (launches) launches[r.id] += 1;
+    }
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  tm.recs.clear();
+  return st;
+}
+
+const char* gla_kernel_name(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= gla::kNumKernels) return "unknown";
+  return kKernelNames[kernel_id];
+}
+
+}  // extern "C"

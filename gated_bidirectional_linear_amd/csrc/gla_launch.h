@@ -1,0 +1,51 @@
+// Internal interface between the C ABI (gla_abi.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+namespace gla {
+
+constexpr int kMaxChunks = 64;   // chunk partials per segment reduced by one tree
+constexpr int kNumKernels = 4;   // rope table, state partials, reduce/prefix, output
+
+// Token partition shared by all kernels of one call.  A segment is the unit of
+// causality: the whole sequence (bidirectional) or one block of latent frames.
+struct Geometry {
+  int T, H, W;
+  int N;        // T*H*W
+  int heads;
+  int d;
+  int seg_len;  // tokens per segment (the last one may be shorter)
+  int nseg;
+  int cps1;     // pass-1 chunks per segment (<= kMaxChunks)
+  int chunk1;   // pass-1 tokens per chunk (multiple of the 64-token tile)
+  int cps2;     // pass-2 chunks per segment
+  int chunk2;   // pass-2 tokens per chunk
+  float eps;
+};
+
+struct LaunchArgs {
+  const void *q, *k, *v, *beta, *g;
+  const float* rms_w;
+  void* out;
+  const float* S_in;  // carried state in (block-causal) or nullptr
+  const float* z_in;
+  float* S_out;       // carried state out (block-causal) or nullptr
+  float* z_out;
+  float2* rope;       // scratch: RoPE table
+  float* partial;     // scratch: [heads][nseg*cps1][d*d + d]
+  float* states;      // scratch: [nseg][heads][d*d + d]
+  bool bf16;
+  hipStream_t stream;
+  Geometry geo;
+};
+
+// Optional per-kernel event timing (instrumentation only).
+struct Timer {
+  virtual void begin(int kernel, hipStream_t s) = 0;
+  virtual void end(int kernel, hipStream_t s) = 0;
+  virtual ~Timer() {}
+};
+
+hipError_t launch_operator(const LaunchArgs& a, Timer& tm);
+
+}  // namespace gla

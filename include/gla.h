@@ -1,0 +1,127 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) gated bidirectional ReLU linear-attention
+ * operator.
+ *
+ * The operation (SANA-Video 2.0 digest, prelims "gated bilinear linear
+ * attention", output formula; SANA-Video notes, key design 1 "RoPE(ReLU(x))",
+ * numerator-only RoPE; reader, appendix F.7 "gated RoPE-rotated linear state"):
+ * for every head, with q^ = q/rms(q), k^ = k/rms(k), phi = ReLU and R_n the 3D
+ * rotary rotation of token n on the (t, y, x) latent grid,
+ *
+ *     S   = sum_n beta_n v_n (R_n phi(k^_n))^T        (d x d, row = v channel)
+ *     z   = sum_n phi(k^_n)                           (d)
+ *     x_j = sigmoid(g_j) * (S R_j phi(q^_j)) / (phi(q^_j) . z + eps)
+ *     out_j = rms_w * x_j / sqrt(mean(x_j^2) + eps)
+ *
+ * The block-causal form (SANA-Video notes, key design 2: cumulative state and
+ * key sum as a constant-memory cache) visits blocks of `block_frames` latent
+ * frames in order; tokens of block b read S and z summed over blocks <= b plus
+ * the carried state passed in.
+ *
+ * Conventions (the pages leave them open; one reading is fixed here):
+ *   - token n = (t*H + y)*W + x, w fastest;
+ *   - q, k, v, g, out: [N, heads, d] contiguous; beta: [N, heads];
+ *     rms_w: [d] fp32 shared by all heads;
+ *   - 3D RoPE: channels [0,d/4) follow t, [d/4,5d/8) follow y, [5d/8,d)
+ *     follow x; pair i of an axis slice is channels (2i,2i+1) and turns by
+ *     pos * 10000^(-2i/d_axis), (u,w) -> (u cos a - w sin a, u sin a + w cos a);
+ *     positions count from 0 in every call;
+ *   - one eps for the q/k RMS normalisation, the denominator and the output
+ *     RMSNorm.
+ *
+ * Pointers: every tensor pointer is a DEVICE pointer, 16-byte aligned.  The
+ * caller owns all buffers; the library keeps no pointer after a call returns.
+ * `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ * are asynchronous: they validate on the host, enqueue kernels on `stream`
+ * and return; the caller synchronises.  Results are bitwise reproducible for
+ * identical inputs and shapes.  On any error nothing is enqueued and no
+ * output is written.  Temporary device memory (RoPE tables, per-chunk partial
+ * states) is taken stream-ordered from the device's default memory pool and
+ * returned on the same stream.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL = -1,          /* a required pointer is NULL */
+  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, eps not finite/positive, size overflow */
+  GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
+  GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
+  GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
+  GLA_ERR_ALLOC = -6,         /* temporary device memory could not be obtained */
+  GLA_ERR_UNSUPPORTED_D = -7, /* head dim not in {32, 64, 128} */
+  GLA_ERR_ALIAS = -8          /* out or the state overlaps another tensor */
+} gla_status;
+
+typedef enum {
+  GLA_DTYPE_F32 = 0,   /* q, k, v, g, beta, out are float32 */
+  GLA_DTYPE_BF16 = 1   /* q, k, v, g, beta, out are bfloat16 (fp32 accumulation inside) */
+} gla_dtype;
+
+/*
+ * Bidirectional operator (SANA-Video 2.0 digest, prelims, output formula:
+ * every token reads the state of all tokens).
+ *
+ *   q, k, v, g : [N, heads, d] in `dtype`, N = T*H*W        (read)
+ *   beta       : [N, heads] in `dtype`, per-token write gate (read)
+ *   rms_w      : [d] float32, output RMSNorm weight          (read)
+ *   out        : [N, heads, d] in `dtype`                    (written; must not alias an input)
+ *   T, H, W    : latent grid (frames, rows, columns), each >= 0; N = 0 is a no-op
+ *   heads      : >= 1;  d : 32, 64 or 128;  eps : finite, > 0
+ * When N == 0 the tensor pointers may be NULL.
+ * Returns GLA_OK or a negative gla_status.
+ */
+int gla_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                const float* rms_w, int T, int H, int W, int heads, int d, float eps,
+                void* out, void* stream, int dtype);
+
+/*
+ * Block-causal operator with a constant-memory carried state (SANA-Video
+ * notes, key design 2).
+ *
+ * Same tensors as gla_forward, plus
+ *   state_S      : [heads, d, d] float32, row = v channel, column = k channel
+ *   state_z      : [heads, d] float32
+ *                  Both are read on entry (zeros = a fresh video) and
+ *                  overwritten with the state after the last block.
+ *   block_frames : latent frames per block, >= 1; the last block may be shorter.
+ * Block b covers frames [b*block_frames, min((b+1)*block_frames, T)); its
+ * tokens read the state inclusive of their own block.  When N == 0 the state
+ * is left unchanged.
+ */
+int gla_block_causal_forward(const void* q, const void* k, const void* v, const void* beta,
+                             const void* g, const float* rms_w, int T, int H, int W, int heads,
+                             int d, float eps, void* out, void* stream, float* state_S,
+                             float* state_z, int block_frames, int dtype);
+
+/* Static text for a gla_status value (never NULL). */
+const char* gla_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int gla_version(void);
+
+/*
+ * Kernel timing instrumentation.  While enabled (on != 0), every call records a
+ * HIP event pair around each of its kernels on the call's stream.
+ * gla_timing_read synchronises on those events, adds the elapsed milliseconds
+ * of all calls made since the previous read into ms[i] and their launch counts
+ * into launches[i] for kernel i < min(n, GLA_NUM_KERNELS), then clears the
+ * record.  Kernel ids: 0 RoPE table, 1 state partials, 2 state reduce/prefix,
+ * 3 fused output.  Timing is process-wide and not thread-safe; turning it on
+ * adds event records to every call.  Returns GLA_OK or GLA_ERR_HIP.
+ */
+#define GLA_NUM_KERNELS 4
+int gla_timing_enable(int on);
+int gla_timing_read(double* ms, long long* launches, int n);
+const char* gla_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

@@ -1,0 +1,71 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}   # max|err| <= TOL * max|ref|
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def gpu_available() -> bool:
+    try:
+        torch = torch_mod()
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def to_device(inp: dict, device="cuda"):
+    """Upload a make_inputs() dict: bf16 from its exact bits, f32 as is."""
+    torch = torch_mod()
+    out = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        if inp["dtype"] == "bf16":
+            bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
+            out[name] = torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        else:
+            out[name] = torch.from_numpy(np.ascontiguousarray(inp[name])).to(device)
+    out["rms_w"] = torch.from_numpy(np.ascontiguousarray(inp["rms_w"], dtype=np.float32)).to(device)
+    return out
+
+
+def to_f64(t) -> np.ndarray:
+    torch = torch_mod()
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got - ref))) / (den if den > 0 else 1.0)
+
+
+def run_forward(dev: dict, grid, eps):
+    import gated_bidirectional_linear_amd as gla
+    torch = torch_mod()
+    out = gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], grid, eps=eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_block_causal(dev: dict, grid, eps, block_frames, S0=None, z0=None):
+    import gated_bidirectional_linear_amd as gla
+    torch = torch_mod()
+    N, heads, d = dev["q"].shape
+    S = torch.zeros((heads, d, d), dtype=torch.float32, device=dev["q"].device)
+    z = torch.zeros((heads, d), dtype=torch.float32, device=dev["q"].device)
+    if S0 is not None:
+        S.copy_(torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)))
+        z.copy_(torch.from_numpy(np.ascontiguousarray(z0, dtype=np.float32)))
+    out = gla.block_causal_forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], grid,
+                                   S, z, block_frames, eps=eps)
+    torch.cuda.synchronize()
+    return out, S, z

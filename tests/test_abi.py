@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/gla.h declares, and rejects bad arguments before touching a GPU.
+No compute call is made here (these tests run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import gated_bidirectional_linear_amd as gla
+from gated_bidirectional_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.gla_version() >> 16 == 1
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
+        s = lib.gla_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.gla_status_string(-99).decode() == "unknown status"
+    names = [lib.gla_kernel_name(i).decode() for i in range(4)]
+    assert names == ["rope_table_kernel", "state_partial_kernel", "state_reduce_kernel", "output_kernel"]
+
+
+# fake, never-dereferenced device addresses, 16-byte aligned and far apart
+A = 1 << 40
+P = [ctypes.c_void_p(A + i * (1 << 36)) for i in range(10)]
+
+
+def fwd(lib, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_forward(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None, dtype)
+
+
+def bc(lib, F=1, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_block_causal_forward(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None,
+                                        p[7], p[8], F, dtype)
+
+
+def test_dtype_and_head_dim_errors(lib):
+    assert fwd(lib, dtype=2) == E_DTYPE
+    assert fwd(lib, dtype=-1) == E_DTYPE
+    for d in (0, 16, 48, 96, 256):
+        assert fwd(lib, d=d) == E_D
+        assert bc(lib, d=d) == E_D
+
+
+def test_shape_errors(lib):
+    assert fwd(lib, T=-1) == E_SHAPE
+    assert fwd(lib, W=-3) == E_SHAPE
+    assert fwd(lib, heads=0) == E_SHAPE
+    for eps in (0.0, -1e-6, math.nan, math.inf):
+        assert fwd(lib, eps=eps) == E_SHAPE
+    assert fwd(lib, T=2000, H=2000, W=2000) == E_SHAPE       # N >= 2^31
+    assert fwd(lib, T=1000, H=1000, W=1000, heads=64, d=128) == E_SHAPE  # N*heads*d >= 2^40
+    assert bc(lib, F=0) == E_SHAPE
+    assert bc(lib, F=-2) == E_SHAPE
+
+
+def test_null_errors(lib):
+    for i in range(7):
+        p = list(P)
+        p[i] = None
+        assert fwd(lib, ptrs=p) == E_NULL, i
+    for i in (7, 8):
+        p = list(P)
+        p[i] = None
+        assert bc(lib, ptrs=p) == E_NULL, i
+
+
+def test_alignment_errors(lib):
+    for i in range(7):
+        p = list(P)
+        p[i] = ctypes.c_void_p(A + i * (1 << 36) + 8)
+        assert fwd(lib, ptrs=p) == E_ALIGN, i
+
+
+def test_alias_errors(lib):
+    for i in range(6):
+        p = list(P)
+        p[6] = p[i]
+        assert fwd(lib, ptrs=p) == E_ALIAS, i
+    p = list(P)
+    p[7] = p[6]          # state_S over out
+    assert bc(lib, ptrs=p) == E_ALIAS
+    p = list(P)
+    p[8] = ctypes.c_void_p(P[7].value + 16)  # state_z inside state_S
+    assert bc(lib, ptrs=p) == E_ALIAS
+
+
+def test_empty_grid_returns_ok_without_device_work(lib):
+    nulls = [None] * 10
+    assert fwd(lib, T=0, ptrs=nulls) == OK
+    assert fwd(lib, T=3, H=0, ptrs=nulls) == OK
+    assert bc(lib, F=2, T=0, ptrs=nulls) == OK
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(32, 2, 32)
+    with pytest.raises(ValueError):
+        gla.forward(q, q, q, torch.zeros(32, 2), q, torch.ones(32), (2, 4, 4))
+
+
+def test_binding_checks_shapes_before_the_device():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(31, 2, 32)
+    with pytest.raises(ValueError):
+        gla.forward(q, q, q, torch.zeros(31, 2), q, torch.ones(32), (2, 4, 4))

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 oracle,
+element by element, on seeded inputs.
+
+Tolerances: max|err| <= 1e-5 * max|ref| for fp32 inputs and <= 2e-2 * max|ref|
+for bf16 inputs with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+import oracle.gla_oracle as orc
+from workloads import WORKLOADS, make_inputs, make_workload_inputs, make_state
+from tests.gpu_helpers import TOL, to_device, to_f64, rel_err, run_forward, run_block_causal
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, **kw):
+    return orc.gla_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"], inp["grid"],
+                           inp["eps"], **kw)
+
+
+def _oracle_bc(inp, F, S0=None, z0=None, **kw):
+    return orc.gla_block_causal_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"],
+                                        inp["grid"], inp["eps"], F, S0=S0, z0=z0, **kw)
+
+
+def _report(name, err, tol):
+    print(f"[parity] {name}: rel err {err:.3e} (tol {tol:.0e})", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wname", ["tiny_f32", "480p", "720p_5s_h20", "720p_5s_h32"])
+def test_bidirectional_workload(wname):
+    w = WORKLOADS[wname]
+    print(f"[case] {wname} grid={w.T}x{w.H}x{w.W} heads={w.heads} d={w.d} {w.dtype}", flush=True)
+    inp = make_workload_inputs(w, seed=0)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    ref = _oracle(inp)
+    err = rel_err(out, ref)
+    _report(wname, err, TOL[w.dtype])
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[w.dtype]
+
+
+def test_block_causal_workload():
+    w = WORKLOADS["block_causal_720p"]
+    print(f"[case] {w.name} F={w.block_frames}", flush=True)
+    inp = make_workload_inputs(w, seed=0)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], w.block_frames)
+    ro, rS, rz = _oracle_bc(inp, w.block_frames)
+    err = rel_err(to_f64(out), ro)
+    _report(w.name, err, TOL[w.dtype])
+    assert err <= TOL[w.dtype]
+    assert rel_err(to_f64(S), rS) <= 1e-2
+    assert rel_err(to_f64(z), rz) <= 1e-5
+
+
+def test_long_sequence_workload_sampled():
+    """720p/60s (N = 159,280, 32 heads) at full size: the oracle evaluates the
+    complete state of 4 heads and the output at 2,048 sampled tokens; every
+    output row is checked for the RMSNorm bound mean((o/w)^2) <= 1."""
+    torch = pytest.importorskip("torch")
+    w = WORKLOADS["720p_60s"]
+    print(f"[case] {w.name} N={w.N} heads={w.heads}", flush=True)
+    inp = make_workload_inputs(w, seed=0)
+    dev = to_device(inp)
+    out = run_forward(dev, inp["grid"], inp["eps"])
+    o32 = out.float()
+    wv = dev["rms_w"][None, None, :]
+    ms = ((o32 / wv) ** 2).mean(dim=-1)
+    assert bool(torch.isfinite(o32).all())
+    assert float(ms.max()) <= 1.0 + 2e-2
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([[0, 1, w.N - 1, w.N - 64], rng.integers(0, w.N, 2044)]))
+    heads = [0, 7, 19, 31]
+    ref = _oracle(inp, heads=heads, rows=rows)
+    got = to_f64(out[torch.from_numpy(rows).cuda()][:, heads, :])
+    err = rel_err(got, ref)
+    _report(w.name + " sampled", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# Shapes: head dims, ragged token counts, tiny grids
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # (T, H, W, heads, d)
+    (2, 4, 4, 2, 32),      # 32 tokens: less than one tile
+    (1, 1, 1, 3, 64),      # a single token
+    (3, 5, 7, 2, 64),      # 105 tokens: ragged tail
+    (5, 9, 13, 3, 128),    # 585 tokens: several tiles + tail
+    (7, 3, 11, 1, 32),     # 231
+    (2, 1, 1, 4, 128),     # 2 tokens
+    (4, 16, 16, 2, 128),   # 1024 tokens: exact tiles
+    (9, 15, 26, 2, 64),    # 3510 tokens
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape, dtype):
+    T, H, W, heads, d = shape
+    print(f"[case] shape {shape} {dtype}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=7)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"{shape} {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("eps", [1e-2, 1.0])
+def test_eps_values(eps):
+    inp = make_inputs(3, 6, 10, 2, 64, "f32", seed=8, eps=eps)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], eps))
+    err = rel_err(out, _oracle(inp))
+    _report(f"eps={eps}", err, TOL["f32"])
+    assert err <= TOL["f32"]
+
+
+def test_degenerate_rows():
+    """All-negative q rows give exactly zero output; zero k rows add nothing."""
+    inp = make_inputs(2, 5, 9, 2, 128, "bf16", seed=9)
+    inp["q"][::5] = -np.abs(inp["q"][::5])
+    inp["k"][1::7] = 0.0
+    from workloads import f32_to_bf16_bits
+    for name in ("q", "k"):
+        inp[name + "_bits"] = f32_to_bf16_bits(inp[name])
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    assert np.all(out[::5] == 0)
+    err = rel_err(out, _oracle(inp))
+    assert err <= TOL["bf16"]
+
+
+def test_zero_beta_gives_zero():
+    inp = make_inputs(2, 4, 9, 2, 64, "f32", seed=10)
+    inp["beta"][:] = 0.0
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    assert np.all(out == 0)
+
+
+def test_deterministic():
+    torch = pytest.importorskip("torch")
+    inp = make_inputs(6, 11, 13, 4, 128, "bf16", seed=11)
+    dev = to_device(inp)
+    a = run_forward(dev, inp["grid"], inp["eps"]).clone()
+    b = run_forward(dev, inp["grid"], inp["eps"])
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_grid_is_noop():
+    torch = pytest.importorskip("torch")
+    inp = make_inputs(0, 4, 4, 2, 64, "bf16", seed=12)
+    dev = to_device(inp)
+    out = run_forward(dev, inp["grid"], inp["eps"])
+    assert out.shape == (0, 2, 64)
+    S0, z0 = make_state(2, 64, seed=1)
+    _, S, z = run_block_causal(dev, inp["grid"], inp["eps"], 2, S0, z0)
+    assert np.array_equal(S.cpu().numpy(), S0) and np.array_equal(z.cpu().numpy(), z0)
+
+
+# ---------------------------------------------------------------------------
+# Block-causal
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,W,heads,d,F", [
+    (7, 3, 5, 2, 64, 2),     # last block shorter
+    (5, 4, 4, 2, 32, 1),     # one frame per block
+    (4, 6, 6, 3, 128, 4),    # F == T: one block
+    (3, 5, 5, 2, 64, 10),    # F > T
+    (9, 8, 9, 2, 128, 3),    # blocks of 216 tokens: tiles straddle nothing
+])
+def test_block_causal_shapes(T, H, W, heads, d, F, dtype):
+    print(f"[case] block-causal {(T, H, W, heads, d, F)} {dtype}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=13)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F)
+    ro, rS, rz = _oracle_bc(inp, F)
+    err = rel_err(to_f64(out), ro)
+    _report(f"bc {(T, H, W, heads, d, F)} {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+    s_tol = 1e-5 if dtype == "f32" else 1e-2
+    assert rel_err(to_f64(S), rS) <= s_tol
+    assert rel_err(to_f64(z), rz) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_causal_with_prior_state(dtype):
+    """The carried state comes from the oracle run over a previous chunk of
+    frames; the second chunk's output must match the one-call oracle."""
+    T1, T2, H, W, heads, d, F = 3, 4, 5, 6, 2, 64, 2
+    full = make_inputs(T1 + T2, H, W, heads, d, dtype, seed=14)
+    hw = H * W
+    first = {k: (v[: T1 * hw] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in full.items()}
+    first["grid"] = (T1, H, W)
+    _, S0, z0 = _oracle_bc(first, F)
+    second = {k: (v[T1 * hw:] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in full.items()}
+    second["grid"] = (T2, H, W)
+    out, S, z = run_block_causal(to_device(second), second["grid"], second["eps"], F, S0, z0)
+    ro, rS, rz = _oracle_bc(second, F, S0=S0, z0=z0)
+    err = rel_err(to_f64(out), ro)
+    _report(f"bc prior state {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+    assert rel_err(to_f64(z), rz) <= 1e-5
+
+
+def test_block_causal_final_state_equals_bidirectional_state():
+    inp = make_inputs(6, 5, 7, 2, 128, "f32", seed=15)
+    _, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], 2)
+    parts = _oracle(inp, return_parts=True)
+    assert rel_err(to_f64(S), parts["S"]) <= 1e-5
+    assert rel_err(to_f64(z), parts["z"]) <= 1e-5
+
+
+def test_block_causal_single_block_equals_bidirectional():
+    torch = pytest.importorskip("torch")
+    inp = make_inputs(4, 5, 6, 2, 64, "bf16", seed=16)
+    dev = to_device(inp)
+    a = to_f64(run_forward(dev, inp["grid"], inp["eps"]))
+    b, _, _ = run_block_causal(dev, inp["grid"], inp["eps"], 4)
+    assert rel_err(to_f64(b), a) <= 1e-2
