@@ -1,0 +1,232 @@
+"""Benchmark of the gated bidirectional ReLU linear-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p_60s]
+
+One step is one full call of the operator (RoPE tables, state partials,
+reduce, fused output) on one seeded synthetic input set already resident in
+HBM.  Prints ONE JSON line on stdout (progress goes to stderr):
+tokens/s for the whole step, achieved HBM GB/s of the step's algorithmic
+bytes, the roofline of the dominant kernel (HIP-event durations taken on the
+call's stream during the timed steps), and the fp64 CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
+KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/gla_kernels.hip",
+                  "gated_bidirectional_linear_amd/csrc/gla_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_alg_bytes(w, kernel: str) -> int:
+    """Algorithmic HBM bytes one launch of a kernel must move."""
+    s = 4 if w.dtype == "f32" else 2
+    big = w.N * w.heads * w.d * s
+    if kernel == "output_kernel":        # read q, g; write out
+        return 3 * big
+    if kernel == "state_partial_kernel":  # read k, v, beta
+        return 2 * big + w.N * w.heads * s
+    return 0
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), stored under profiles/.
+    None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, heads_sample: int):
+    """Time the fp64 oracle on `heads_sample` heads of the full workload (all
+    tokens, complete state and output) and scale to the whole workload."""
+    import numpy as np
+    import oracle.gla_oracle as orc
+    from workloads import head_slice_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    heads = list(range(min(heads_sample, w.heads)))
+    sub = head_slice_f32(inp, heads) if w.dtype == "bf16" else {
+        **inp, **{n: inp[n][:, heads] for n in ("q", "k", "v", "g", "beta")}}
+    t0 = time.perf_counter()
+    orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"], sub["eps"])
+    dt = time.perf_counter() - t0
+    per_call = dt * w.heads / len(heads)
+    return {
+        "value": w.N / per_call,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(heads)} of {w.heads} heads at full N={w.N} (whole state and output), "
+                  f"{dt:.2f} s, scaled x{w.heads / len(heads):g} to the full workload",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="720p_60s")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this operator's path is measured per GPU "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_bidirectional_linear_amd as gla
+    from workloads import WORKLOADS, make_workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: grid {w.T}x{w.H}x{w.W} N={w.N} heads={w.heads} d={w.d} {w.dtype}")
+    t0 = time.time()
+    inp = make_workload_inputs(w, seed=args.seed, keep_f32=(w.dtype == "f32"))
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f} s")
+
+    def upload(name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(inp[name]).to(dev)
+
+    # Working sets that would sit in the 256 MB Infinity Cache are rotated over
+    # enough copies (> 1 GB total) that each step reads from HBM.
+    sets = max(1, -(-1_000_000_000 // w.alg_bytes())) if w.alg_bytes() < 1_000_000_000 else 1
+    bufs = []
+    for i in range(sets):
+        t = {n: upload(n) for n in ("q", "k", "v", "g", "beta")}
+        t["out"] = torch.empty_like(t["q"])
+        bufs.append(t)
+    rms_w = torch.from_numpy(inp["rms_w"]).to(dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {sets} input set(s) resident on {torch.cuda.get_device_name(dev)}")
+
+    def step(i):
+        b = bufs[i % sets]
+        gla.forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, (w.T, w.H, w.W), eps=w.eps, out=b["out"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gla.timing_read()            # discard anything recorded before
+    gla.timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    gla.timing_enable(False)
+    kt = gla.timing_read()
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    ms_step = elapsed * 1e3 / args.steps
+    tokens_s = w.N / (ms_step * 1e-3)
+    step_gbps = w.alg_bytes() / (ms_step * 1e-3) / 1e9
+    kernels = {k: {"ms_per_launch": (ms / n if n else None), "launches": n} for k, (ms, n) in kt.items()}
+    dom = max(("state_partial_kernel", "output_kernel"), key=lambda k: kt[k][0])
+    dom_ms = kt[dom][0] / max(1, kt[dom][1])
+    achieved = kernel_alg_bytes(w, dom) / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(dom, w.name)
+    for k, v in kernels.items():
+        log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on {args.cpu_heads} heads ...")
+        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        log(f"[bench] oracle: {cpu['value']:.1f} tokens/s ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q,k,v,g; beta=sigmoid(N(0,1)); rms_w=1+0.1N(0,1))",
+        "config": {
+            "workload": w.name,
+            "grid": f"{w.T}x{w.H}x{w.W}",
+            "tokens": w.N,
+            "heads": w.heads,
+            "head_dim": w.d,
+            "eps": w.eps,
+            "mode": "bidirectional" if w.block_frames is None else f"block-causal F={w.block_frames}",
+            "input_sets": sets,
+        },
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "alg_bytes_per_step": w.alg_bytes(),
+        "kernels": kernels,
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -41,18 +41,35 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   const int tiles_per_seg = ceil_div(G.seg_len, kTile);
   const int per_seg_heads = heads * G.nseg;
 
+  // RoPE rows a chunk of L tokens needs in LDS: the y and x blocks plus the
+  // frames it can span (at worst alignment).
+  const int HW = H * W;
+  const long yx = (long)H * (3 * d / 16) + (long)W * (3 * d / 16);
+  auto rope_fits = [&](long L) {
+    long frames = (L + HW - 2) / HW + 1;
+    if (frames > T) frames = T;
+    return yx + frames * (d / 8) <= gla::kRopeLdsEntries;
+  };
+
   const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", kDefaultTargetWg1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
+  // more (smaller) chunks when a chunk's RoPE rows would not fit in LDS
+  while (!rope_fits((long)ceil_div(tiles_per_seg, cps1) * kTile) && cps1 < gla::kMaxChunks && cps1 < tiles_per_seg)
+    ++cps1;
   G.chunk1 = ceil_div(tiles_per_seg, cps1) * kTile;
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
+  G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
 
   const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", kDefaultTargetWg2), per_seg_heads);
   int cps2 = want2 < 1 ? 1 : want2;
   if (cps2 > tiles_per_seg) cps2 = tiles_per_seg;
+  while (!rope_fits((long)ceil_div(tiles_per_seg, cps2) * kTile) && cps2 < tiles_per_seg) ++cps2;
   G.chunk2 = ceil_div(tiles_per_seg, cps2) * kTile;
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
+  G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
+  if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
   return G;
 }
 

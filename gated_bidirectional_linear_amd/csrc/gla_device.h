@@ -34,6 +34,16 @@ template <typename E> struct Elem;
 
 template <> struct Elem<float> {
   static constexpr bool is_bf16 = false;
+  struct Raw { f32x4 a, b; };  // 8 channels as loaded
+  __device__ __forceinline__ static Raw load_raw(const float* p) {
+    Raw r;
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+    return r;
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, float (&x)[8]) {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w; x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+  }
   __device__ __forceinline__ static void load8(const float* p, float (&x)[8]) {
     const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
     const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
@@ -50,6 +60,14 @@ template <> struct Elem<float> {
 
 template <> struct Elem<bf16_t> {
   static constexpr bool is_bf16 = true;
+  typedef u32x4 Raw;  // 8 channels as loaded
+  __device__ __forceinline__ static Raw load_raw(const bf16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ static void unpack(const Raw& u, float (&x)[8]) {
+    x[0] = bf16lo(u.x); x[1] = bf16hi(u.x); x[2] = bf16lo(u.y); x[3] = bf16hi(u.y);
+    x[4] = bf16lo(u.z); x[5] = bf16hi(u.z); x[6] = bf16lo(u.w); x[7] = bf16hi(u.w);
+  }
   __device__ __forceinline__ static void load8(const bf16_t* p, float (&x)[8]) {
     const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     x[0] = bf16lo(u.x); x[1] = bf16hi(u.x); x[2] = bf16lo(u.y); x[3] = bf16hi(u.y);
@@ -63,6 +81,17 @@ template <> struct Elem<bf16_t> {
     return __uint_as_float(((uint32_t)*p) << 16);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes every wave wait for its outstanding global loads (the
+// prefetched next tile) at each barrier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---------------------------------------------------------------------------
 // Sum over groups of L consecutive lanes (L = 4, 8 or 16), result in every lane
@@ -131,24 +160,81 @@ struct Rope {
   static constexpr int PT = D / 8;        // pairs on the t axis
   static constexpr int PY = 3 * D / 16;   // pairs on the y axis
   static constexpr int PX = 3 * D / 16;   // pairs on the x axis
-  // rotate the 4 pairs held by a thread (channels 8cg..8cg+7) of token (t,y,x)
-  __device__ __forceinline__ static void rotate(float (&x)[8], int cg, int t, int y, int xx,
-                                                const float2* __restrict__ tab, int T, int H) {
-    const float2* tab_t = tab;
-    const float2* tab_y = tab + (size_t)T * PT;
-    const float2* tab_x = tab_y + (size_t)H * PY;
+  // Every thread holds channels 8cg..8cg+7 = pairs 4cg..4cg+3.  When the axis
+  // boundaries are multiples of 4 pairs (d = 64, 128) those 4 pairs share an
+  // axis and sit next to each other in its table: two 16-byte reads.
+  static constexpr bool kGrouped = (PT % 4 == 0) && (PY % 4 == 0);
+
+  // A view of the table: frames [t_lo, t_lo + nt) of the t block, then the
+  // whole y block [H][PY] and x block [W][PX].  The global table is the view
+  // with t_lo = 0, nt = T; the LDS copy holds only the frames a chunk spans.
+  struct View {
+    const float2* tab;
+    int t_lo, nt, H;
+    // float2 offset of pair p of a token at (t, y, x)
+    __device__ __forceinline__ int offset(int p, int t, int y, int x) const {
+      const int axis = (p < PT) ? 0 : ((p < PT + PY) ? 1 : 2);
+      const int pos = axis == 0 ? (t - t_lo) : (axis == 1 ? y : x);
+      const int base = axis == 0 ? p : (axis == 1 ? nt * PT + (p - PT) : nt * PT + H * PY + (p - PT - PY));
+      const int stride = axis == 0 ? PT : (axis == 1 ? PY : PX);
+      return base + pos * stride;
+    }
+  };
+
+  struct CS { float c[4], s[4]; };
+
+  __device__ __forceinline__ static CS fetch(const View& v, int cg, int t, int y, int x) {
+    CS r;
+    if constexpr (kGrouped) {
+      const f32x4* e = reinterpret_cast<const f32x4*>(v.tab + v.offset(4 * cg, t, y, x));
+      const f32x4 a = e[0], b = e[1];
+      r.c[0] = a.x; r.s[0] = a.y; r.c[1] = a.z; r.s[1] = a.w;
+      r.c[2] = b.x; r.s[2] = b.y; r.c[3] = b.z; r.s[3] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 cs = v.tab[v.offset(4 * cg + j, t, y, x)];
+        r.c[j] = cs.x;
+        r.s[j] = cs.y;
+      }
+    }
+    return r;
+  }
+
+  // (u, w) -> (u cos - w sin, u sin + w cos) on each of the 4 pairs
+  __device__ __forceinline__ static void apply(float (&x)[8], const CS& cs) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int p = 4 * cg + j;
-      const float2* e;
-      if (p < PT) e = tab_t + t * PT + p;
-      else if (p < PT + PY) e = tab_y + y * PY + (p - PT);
-      else e = tab_x + xx * PX + (p - PT - PY);
-      const float2 cs = *e;
       const float u = x[2 * j], w = x[2 * j + 1];
-      x[2 * j] = u * cs.x - w * cs.y;
-      x[2 * j + 1] = u * cs.y + w * cs.x;
+      x[2 * j] = u * cs.c[j] - w * cs.s[j];
+      x[2 * j + 1] = u * cs.s[j] + w * cs.c[j];
     }
+  }
+
+  // Copy the frames [t_lo, t_lo + nt) and the y/x blocks of the global table
+  // into LDS (all kThreads threads take part; caller synchronises).  At most
+  // kMaxEntries entries; every thread issues its loads together (indices
+  // past the end are clamped to entry 0 and not stored).
+  template <int kMaxEntries>
+  __device__ __forceinline__ static View stage(float2* lds, const float2* __restrict__ tab, int T, int H, int W,
+                                               int t_lo, int nt) {
+    constexpr int PER = kMaxEntries / kThreads;
+    static_assert(kMaxEntries % kThreads == 0, "staging split");
+    const int n_t = nt * PT;
+    const int total = n_t + H * PY + W * PX;
+    float2 tmp[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      const int src = (i < n_t) ? t_lo * PT + i : T * PT + (i - n_t);
+      tmp[j] = tab[i < total ? src : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      if (i < total) lds[i] = tmp[j];
+    }
+    return View{lds, t_lo, nt, H};
   }
 };
 

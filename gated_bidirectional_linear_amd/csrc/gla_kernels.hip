@@ -75,16 +75,27 @@ __device__ __forceinline__ Chunk chunk_of(int lin, const Geometry& G, int cps, i
   return c;
 }
 
-// Load 8 channels of TPT consecutive tokens of one head; zero-fill past `end`.
+// Issue the loads of 8 channels of TPT consecutive tokens of one head.  Rows
+// at or past `end` are clamped to the last valid row (end > n0 is guaranteed
+// by the callers) so every load is unconditional and all of them are in
+// flight together; the clamped rows are zeroed when unpacked.
 template <int D, typename E, int TPT>
-__device__ __forceinline__ void load_rows(const E* __restrict__ base, long n0, long end, int heads, int head,
-                                          int cg, float (&x)[TPT][8]) {
+__device__ __forceinline__ void issue_rows(const E* __restrict__ base, long n0, long end, int heads, int head,
+                                           int cg, typename Elem<E>::Raw (&r)[TPT]) {
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    const long n = n0 + i;
-    if (n < end) {
-      Elem<E>::load8(base + ((size_t)n * heads + head) * D + 8 * cg, x[i]);
-    } else {
+    const long n = min(n0 + i, end - 1);
+    r[i] = Elem<E>::load_raw(base + ((size_t)n * heads + head) * D + 8 * cg);
+  }
+}
+
+template <typename E, int TPT>
+__device__ __forceinline__ void unpack_rows(const typename Elem<E>::Raw (&r)[TPT], long n0, long end,
+                                            float (&x)[TPT][8]) {
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    Elem<E>::unpack(r[i], x[i]);
+    if (n0 + i >= end) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) x[i][c] = 0.f;
     }
@@ -135,13 +146,28 @@ __device__ __forceinline__ void store_tcol(E* dst, const float (&x)[TPT][8], int
   }
 }
 
-template <int D, typename E>
+// Stage the RoPE rows of the frames a chunk spans (or use the global table).
+template <int D, bool LDSR>
+__device__ __forceinline__ typename Rope<D>::View rope_view(float2* lds, const float2* __restrict__ rope,
+                                                            const Geometry& G, long begin, long end) {
+  if constexpr (LDSR) {
+    const int HW = G.H * G.W;
+    const int t_lo = begin < end ? (int)(begin / HW) : 0;
+    const int nt = begin < end ? (int)((end - 1) / HW) - t_lo + 1 : 0;
+    return Rope<D>::template stage<kRopeLdsEntries>(lds, rope, G.T, G.H, G.W, t_lo, nt);
+  } else {
+    return typename Rope<D>::View{rope, 0, G.T, G.H};
+  }
+}
+
+template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   using C = PartialCfg<D, E>;
   using M = Mfma<E>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
   E* rkT = reinterpret_cast<E*>(smem);          // [D][PITCH]  (k channel, token)
   E* vT = rkT + D * C::PITCH;                   // [D][PITCH]  (v channel, token)
 
@@ -163,15 +189,43 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
 
+  typename Elem<E>::Raw kr[C::TPT], vr[C::TPT];
+  E br[C::TPT];   // raw: converted only when the tile is consumed
+  auto issue = [&](long t0) {
+    const long n0 = t0 + (long)tg * C::TPT;
+    issue_rows<D, E, C::TPT>(k, n0, ch.end, G.heads, ch.head, cg, kr);
+    issue_rows<D, E, C::TPT>(v, n0, ch.end, G.heads, ch.head, cg, vr);
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i)
+      br[i] = beta[(size_t)min(n0 + i, ch.end - 1) * G.heads + ch.head];
+  };
+  const typename Rope<D>::View rv =
+      rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  if (ch.begin < ch.end) issue(ch.begin);
+  if constexpr (LDSR) lds_barrier();
+
   for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
     const long n0 = t0 + (long)tg * C::TPT;
     float kx[C::TPT][8], vx[C::TPT][8];
     float bt[C::TPT];
-    load_rows<D, E, C::TPT>(k, n0, ch.end, G.heads, ch.head, cg, kx);
-    load_rows<D, E, C::TPT>(v, n0, ch.end, G.heads, ch.head, cg, vx);
+    unpack_rows<E, C::TPT>(kr, n0, ch.end, kx);
+    unpack_rows<E, C::TPT>(vr, n0, ch.end, vx);
 #pragma unroll
-    for (int i = 0; i < C::TPT; ++i)
-      bt[i] = (n0 + i < ch.end) ? Elem<E>::load1(beta + (size_t)(n0 + i) * G.heads + ch.head) : 0.f;
+    for (int i = 0; i < C::TPT; ++i) bt[i] = (n0 + i < ch.end) ? Elem<E>::load1(&br[i]) : 0.f;
+    // RoPE entries of this tile are requested before the next tile's rows so
+    // that waiting for them (in-order counter) does not wait for the prefetch.
+    typename Rope<D>::CS cs[C::TPT];
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int n = (int)min(n0 + i, (long)G.N - 1);
+      const int t = n / HW;
+      const int rem = n - t * HW;
+      const int y = rem / G.W;
+      cs[i] = Rope<D>::fetch(rv, cg, t, y, rem - y * G.W);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t0 + kTile < ch.end) issue(t0 + kTile);   // prefetch the next tile
+    __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
@@ -186,12 +240,7 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
         kx[i][c] = p;
         zacc[c] += p;
       }
-      const long n = min(n0 + i, (long)G.N - 1);
-      const int t = (int)(n / HW);
-      const int rem = (int)(n - (long)t * HW);
-      const int y = rem / G.W;
-      const int xx = rem - y * G.W;
-      Rope<D>::rotate(kx[i], cg, t, y, xx, rope, G.T, G.H);
+      Rope<D>::apply(kx[i], cs[i]);
 #pragma unroll
       for (int c = 0; c < 8; ++c) kx[i][c] *= bt[i];
     }
@@ -202,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
       store_tcol<E, C::TPT>(rkT + (8 * cg + c) * C::PITCH + col, kx, c);
       store_tcol<E, C::TPT>(vT + (8 * cg + c) * C::PITCH + col, vx, c);
     }
-    __syncthreads();
+    lds_barrier();
 
     const int lrow = lane & 31;
     const int lk = M::KPL * (lane >> 5);
@@ -230,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
         acc[0] = M::mma(a, b, acc[0]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   float* dst = partial + ((size_t)ch.head * G.nseg * G.cps1 + ch.index) * (size_t)(D * D + D);
@@ -239,13 +288,13 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
   float* zred = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int c = 0; c < 8; ++c) zred[tg * D + 8 * cg + c] = zacc[c];
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     float s = 0.f;
     for (int gi = 0; gi < C::TG; ++gi) s += zred[gi * D + tid];
     dst[D * D + tid] = s;
   }
-  __syncthreads();
+  lds_barrier();
 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
@@ -253,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     float* kred = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int r = 0; r < 16; ++r) kred[(wave * 16 + r) * 64 + lane] = acc[0][r];
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -331,7 +380,7 @@ struct OutputCfg {
   static constexpr int SMEM = RQ_BYTES > NUM_BYTES ? RQ_BYTES : NUM_BYTES;
 };
 
-template <int D, typename E>
+template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void output_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ rms_w, const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
@@ -339,7 +388,8 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   using M = Mfma<E>;
   constexpr int KSTEPS = D / M::KSTEP;
   constexpr int SZ = D * D + D;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
   E* rqs = reinterpret_cast<E*>(smem);            // [kTile][RQ_PITCH]  (token, k channel)
   float* nums = reinterpret_cast<float*>(smem);   // [kTile][NUM_PITCH] (token, v channel)
 
@@ -375,12 +425,35 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
     wc[c] = rms_w[8 * cg + c];
   }
 
+  typename Elem<E>::Raw qr[C::TPT], gr[C::TPT];
+  auto issue = [&](long t0) {
+    const long n0 = t0 + (long)tg * C::TPT;
+    issue_rows<D, E, C::TPT>(q, n0, ch.end, G.heads, ch.head, cg, qr);
+    issue_rows<D, E, C::TPT>(g, n0, ch.end, G.heads, ch.head, cg, gr);
+  };
+  const typename Rope<D>::View rv =
+      rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  if (ch.begin < ch.end) issue(ch.begin);
+  if constexpr (LDSR) lds_barrier();
+
   for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
     const long n0 = t0 + (long)tg * C::TPT;
     float qx[C::TPT][8], gx[C::TPT][8];
     float rden[C::TPT];
-    load_rows<D, E, C::TPT>(q, n0, ch.end, G.heads, ch.head, cg, qx);
-    load_rows<D, E, C::TPT>(g, n0, ch.end, G.heads, ch.head, cg, gx);
+    unpack_rows<E, C::TPT>(qr, n0, ch.end, qx);
+    unpack_rows<E, C::TPT>(gr, n0, ch.end, gx);
+    typename Rope<D>::CS cs[C::TPT];
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      const int n = (int)min(n0 + i, (long)G.N - 1);
+      const int t = n / HW;
+      const int rem = n - t * HW;
+      const int y = rem / G.W;
+      cs[i] = Rope<D>::fetch(rv, cg, t, y, rem - y * G.W);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t0 + kTile < ch.end) issue(t0 + kTile);   // prefetch the next tile
+    __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
@@ -398,12 +471,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       }
       dp = group_sum<C::CG>(dp);
       rden[i] = 1.0f / (dp + G.eps);
-      const long n = min(n0 + i, (long)G.N - 1);
-      const int t = (int)(n / HW);
-      const int rem = (int)(n - (long)t * HW);
-      const int y = rem / G.W;
-      const int xx = rem - y * G.W;
-      Rope<D>::rotate(qx[i], cg, t, y, xx, rope, G.T, G.H);
+      Rope<D>::apply(qx[i], cs[i]);
       E* dst = rqs + (tg * C::TPT + i) * C::RQ_PITCH + 8 * cg;
       if constexpr (Elem<E>::is_bf16) {
         uint4 u;
@@ -417,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
 #pragma unroll
       for (int c = 0; c < 8; ++c) gx[i][c] = 1.0f / (1.0f + __expf(-gx[i][c]));
     }
-    __syncthreads();
+    lds_barrier();
 
     f32x16 acc[C::PPW];
     if (wave < C::ACTIVE) {
@@ -433,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave < C::ACTIVE) {
 #pragma unroll
       for (int u = 0; u < C::PPW; ++u) {
@@ -445,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
               make_float4(acc[u][4 * rb], acc[u][4 * rb + 1], acc[u][4 * rb + 2], acc[u][4 * rb + 3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
@@ -466,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       const long n = n0 + i;
       if (n < ch.end) Elem<E>::store8(out + ((size_t)n * G.heads + ch.head) * D + 8 * cg, x);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -489,8 +557,12 @@ static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
   {
     const int blocks = G.heads * G.nseg * G.cps1;
     tm.begin(1, st);
-    hipLaunchKernelGGL((state_partial_kernel<D, E>), dim3(blocks), dim3(kThreads), 0, st,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
+    if (G.rope_lds1)
+      hipLaunchKernelGGL((state_partial_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, st,
+                         (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
+    else
+      hipLaunchKernelGGL((state_partial_kernel<D, E, false>), dim3(blocks), dim3(kThreads), 0, st,
+                         (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
     tm.end(1, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -508,8 +580,12 @@ static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
   {
     const int blocks = G.heads * G.nseg * G.cps2;
     tm.begin(3, st);
-    hipLaunchKernelGGL((output_kernel<D, E>), dim3(blocks), dim3(kThreads), 0, st, (const E*)a.q, (const E*)a.g,
-                       (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+    if (G.rope_lds2)
+      hipLaunchKernelGGL((output_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, st, (const E*)a.q,
+                         (const E*)a.g, (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+    else
+      hipLaunchKernelGGL((output_kernel<D, E, false>), dim3(blocks), dim3(kThreads), 0, st, (const E*)a.q,
+                         (const E*)a.g, (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
     tm.end(3, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

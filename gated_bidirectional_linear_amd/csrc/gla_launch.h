@@ -6,6 +6,7 @@ namespace gla {
 
 constexpr int kMaxChunks = 64;   // chunk partials per segment reduced by one tree
 constexpr int kNumKernels = 4;   // rope table, state partials, reduce/prefix, output
+constexpr int kRopeLdsEntries = 2048;  // float2 entries of RoPE table a workgroup may stage in LDS (16 KB)
 
 // Token partition shared by all kernels of one call.  A segment is the unit of
 // causality: the whole sequence (bidirectional) or one block of latent frames.
@@ -20,6 +21,8 @@ struct Geometry {
   int chunk1;   // pass-1 tokens per chunk (multiple of the 64-token tile)
   int cps2;     // pass-2 chunks per segment
   int chunk2;   // pass-2 tokens per chunk
+  int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
+  int rope_lds2;  // same for pass 2
   float eps;
 };
 

@@ -222,3 +222,38 @@ def test_block_causal_single_block_equals_bidirectional():
     a = to_f64(run_forward(dev, inp["grid"], inp["eps"]))
     b, _, _ = run_block_causal(dev, inp["grid"], inp["eps"], 4)
     assert rel_err(to_f64(b), a) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# Launch-plan variants: RoPE rows from the global table instead of LDS, grids
+# too large for the LDS table, and different chunk counts.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_global_rope_table_path(monkeypatch, dtype):
+    monkeypatch.setenv("GLA_ROPE_GLOBAL", "1")
+    inp = make_inputs(5, 9, 13, 3, 128, dtype, seed=17)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"global rope {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+
+
+def test_large_frame_grid_falls_back_to_global_table():
+    """64x64 latent pixels per frame: the y/x RoPE blocks exceed the LDS budget."""
+    inp = make_inputs(2, 64, 64, 2, 128, "bf16", seed=18)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report("64x64 frame", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("wg1,wg2", [("1", "1"), ("4096", "65536"), ("37", "300")])
+def test_chunking_variants(monkeypatch, wg1, wg2):
+    monkeypatch.setenv("GLA_PASS1_WORKGROUPS", wg1)
+    monkeypatch.setenv("GLA_PASS2_WORKGROUPS", wg2)
+    inp = make_inputs(7, 11, 13, 2, 64, "bf16", seed=19)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"chunking {wg1}/{wg2}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]

@@ -10,11 +10,11 @@ Workload shapes follow the pages' video-latent grids (SANA-Video 2.0 digest,
 attention): 480p/81 frames is an 11x15x26 latent grid (4,290 tokens), 720p is
 22x40 latent pixels per frame, and 60 s at 24 fps gives 181 latent frames.
 
-Draw recipe (fixed order, one ``numpy.random.default_rng(seed)`` stream):
-q, k, v, g ~ N(0,1) fp32, then beta-logits ~ N(0,1) fp32, then rms_w noise
-~ N(0,1) fp32.  beta = sigmoid(logit), rms_w = 1 + 0.1*noise.  For bf16
-workloads every tensor handed to the operator (q, k, v, g, beta) is rounded
-to bfloat16 with round-to-nearest-even; rms_w stays fp32.
+Draw recipe: q, k, v, g ~ N(0,1) fp32, beta = sigmoid(N(0,1)), rms_w =
+1 + 0.1*N(0,1) fp32, every tensor from its own counter-keyed PCG64 streams
+(see make_inputs).  For bf16 workloads every tensor handed to the operator
+(q, k, v, g, beta) is rounded to bfloat16 with round-to-nearest-even; rms_w
+stays fp32.
 """
 from __future__ import annotations
 
@@ -83,8 +83,11 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -98,40 +101,107 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(f32_to_bf16_bits(x))
 
 
+_BLOCK = 1 << 22          # elements per independently seeded block
+_STREAMS = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "rms_w": 5}
+
+
+def _normal_block(seed: int, stream: int, block: int, n: int) -> np.ndarray:
+    ss = np.random.SeedSequence(seed, spawn_key=(stream, block))
+    return np.random.Generator(np.random.PCG64(ss)).standard_normal(n, dtype=np.float32)
+
+
+def _workers() -> int:
+    try:
+        import os
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = 4
+    return max(1, min(16, n))
+
+
+def _draw(seed: int, name: str, shape, dtype: str, keep_f32: bool, pool, sigmoid: bool = False):
+    size = int(np.prod(shape))
+    f32 = np.empty(size, np.float32) if (keep_f32 or dtype == "f32") else None
+    bits = np.empty(size, np.uint16) if dtype == "bf16" else None
+    stream = _STREAMS[name]
+
+    def work(b):
+        lo = b * _BLOCK
+        hi = min(size, lo + _BLOCK)
+        x = _normal_block(seed, stream, b, hi - lo)
+        if sigmoid:
+            x = (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+        if bits is not None:
+            bb = f32_to_bf16_bits(x)
+            bits[lo:hi] = bb
+            if f32 is not None:
+                f32[lo:hi] = bf16_bits_to_f32(bb)
+        else:
+            f32[lo:hi] = x
+
+    nblocks = (size + _BLOCK - 1) // _BLOCK
+    if pool is None or nblocks <= 1:
+        for b in range(nblocks):
+            work(b)
+    else:
+        list(pool.map(work, range(nblocks)))
+    return (None if f32 is None else f32.reshape(shape)), (None if bits is None else bits.reshape(shape))
+
+
 def make_inputs(T: int, H: int, W: int, heads: int, d: int, dtype: str, seed: int = 0,
-                eps: float = 1e-6) -> dict:
+                eps: float = 1e-6, keep_f32: bool = True) -> dict:
     """Draw one seeded input set.
 
     Returns a dict with fp32 numpy arrays ``q, k, v, g`` of shape [N, heads, d],
     ``beta`` [N, heads], ``rms_w`` [d], plus ``eps``, ``grid`` (T, H, W) and
     ``dtype``.  For dtype "bf16" the fp32 arrays hold exactly the bf16 values
-    the operator receives, and ``*_bits`` (uint16) hold their storage.
+    the operator receives, and ``*_bits`` (uint16) hold their storage;
+    with keep_f32=False only the bits are kept (large workloads).
+
+    Each tensor is filled in row-major order in blocks of 2^22 elements; block
+    b of tensor t (q, k, v, g, beta-logit, rms_w-noise = 0..5) is drawn from
+    PCG64(SeedSequence(seed, spawn_key=(t, b))), so the values do not depend
+    on how many threads draw them.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"unknown dtype {dtype!r}")
     N = T * H * W
-    rng = np.random.default_rng(seed)
-    shape = (N, heads, d)
+    from concurrent.futures import ThreadPoolExecutor
     out = {}
-    for name in ("q", "k", "v", "g"):
-        out[name] = rng.standard_normal(shape, dtype=np.float32)
-    logits = rng.standard_normal((N, heads), dtype=np.float32)
-    out["beta"] = (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
-    noise = rng.standard_normal(d, dtype=np.float32)
+    big = N * heads * d > 2 * _BLOCK
+    pool = ThreadPoolExecutor(_workers()) if big else None
+    try:
+        for name in ("q", "k", "v", "g"):
+            f, b = _draw(seed, name, (N, heads, d), dtype, keep_f32, pool)
+            out[name] = f
+            if b is not None:
+                out[name + "_bits"] = b
+        f, b = _draw(seed, "beta", (N, heads), dtype, keep_f32, pool, sigmoid=True)
+        out["beta"] = f
+        if b is not None:
+            out["beta_bits"] = b
+    finally:
+        if pool is not None:
+            pool.shutdown()
+    noise = _normal_block(seed, _STREAMS["rms_w"], 0, d)
     out["rms_w"] = (1.0 + 0.1 * noise.astype(np.float64)).astype(np.float32)
-    if dtype == "bf16":
-        for name in ("q", "k", "v", "g", "beta"):
-            bits = f32_to_bf16_bits(out[name])
-            out[name + "_bits"] = bits
-            out[name] = bf16_bits_to_f32(bits)
     out["eps"] = float(eps)
     out["grid"] = (T, H, W)
     out["dtype"] = dtype
     return out
 
 
-def make_workload_inputs(w: Workload, seed: int = 0) -> dict:
-    return make_inputs(w.T, w.H, w.W, w.heads, w.d, w.dtype, seed=seed, eps=w.eps)
+def make_workload_inputs(w: Workload, seed: int = 0, keep_f32: bool = True) -> dict:
+    return make_inputs(w.T, w.H, w.W, w.heads, w.d, w.dtype, seed=seed, eps=w.eps, keep_f32=keep_f32)
+
+
+def head_slice_f32(inp: dict, heads) -> dict:
+    """fp32 copies of the listed heads of a bits-only bf16 input set."""
+    out = dict(inp)
+    for name in ("q", "k", "v", "g"):
+        out[name] = bf16_bits_to_f32(inp[name + "_bits"][:, heads, :])
+    out["beta"] = bf16_bits_to_f32(inp["beta_bits"][:, heads])
+    return out
 
 
 def make_state(heads: int, d: int, seed: int, scale: float = 1.0) -> tuple:
