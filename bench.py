@@ -25,8 +25,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
-KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/gla_kernels.hip",
-                  "gated_bidirectional_linear_amd/csrc/gla_device.h"]
+KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
+                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
 
 
 def log(*a):

@@ -20,6 +20,8 @@ constexpr int kTile = 64;
 // workgroup, so it stays near two per CU (256 CUs); pass 2 has no such cost
 // and takes more for load balance.  Overridable for tuning sweeps.
 constexpr int kDefaultTargetWg1 = 512;
+// The fragment-built pass-1 kernel (bf16, d = 128) runs two workgroups per CU.
+constexpr int kDefaultTargetWgReg1 = 512;
 constexpr int kDefaultTargetWg2 = 2048;
 
 int env_int(const char* name, int dflt) {
@@ -31,7 +33,7 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames) {
+Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames, bool bf16) {
   Geometry G{};
   G.T = T; G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
   G.N = T * H * W;
@@ -51,7 +53,11 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
     return yx + frames * (d / 8) <= gla::kRopeLdsEntries;
   };
 
-  const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", kDefaultTargetWg1), per_seg_heads);
+  // buffer-load offsets of the fragment-built kernel are 32-bit
+  const bool small = (long long)T * H * W * heads * d * 2 < (1LL << 31);
+  G.pass1_reg = (bf16 && d == 128 && small && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
+  const int target1 = G.pass1_reg ? kDefaultTargetWgReg1 : kDefaultTargetWg1;
+  const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
@@ -189,7 +195,7 @@ int run(const void* q, const void* k, const void* v, const void* beta, const voi
   const long long N = (long long)T * H * W;
   if (N == 0) return GLA_OK;
 
-  const Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0);
+  const Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0, dtype == GLA_DTYPE_BF16);
   const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);

@@ -1,0 +1,73 @@
+// Device code shared by the operator's kernels: chunk geometry, batched row
+// loads and the RoPE table view.
+#pragma once
+#include "gla_device.h"
+#include "gla_launch.h"
+
+namespace gla {
+
+// ===========================================================================
+// Chunk geometry shared by the kernels (all integer arithmetic, no tables)
+// ===========================================================================
+struct Chunk {
+  long begin, end;  // token range [begin, end)
+  int head, seg, index;
+};
+
+__device__ __forceinline__ Chunk chunk_of(int lin, const Geometry& G, int cps, int chunk_len) {
+  Chunk c;
+  const int per_head = G.nseg * cps;
+  c.head = lin / per_head;
+  const int ci = lin - c.head * per_head;
+  c.seg = ci / cps;
+  c.index = ci;
+  const int j = ci - c.seg * cps;
+  const long s0 = (long)c.seg * G.seg_len;
+  const long s1 = min(s0 + (long)G.seg_len, (long)G.N);
+  c.begin = min(s0 + (long)j * chunk_len, s1);
+  c.end = min(c.begin + (long)chunk_len, s1);
+  return c;
+}
+
+// Issue the loads of 8 channels of TPT consecutive tokens of one head.  Rows
+// at or past `end` are clamped to the last valid row (end > n0 is guaranteed
+// by the callers) so every load is unconditional and all of them are in
+// flight together; the clamped rows are zeroed when unpacked.
+template <int D, typename E, int TPT>
+__device__ __forceinline__ void issue_rows(const E* __restrict__ base, long n0, long end, int heads, int head,
+                                           int cg, typename Elem<E>::Raw (&r)[TPT]) {
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const long n = min(n0 + i, end - 1);
+    r[i] = Elem<E>::load_raw(base + ((size_t)n * heads + head) * D + 8 * cg);
+  }
+}
+
+template <typename E, int TPT>
+__device__ __forceinline__ void unpack_rows(const typename Elem<E>::Raw (&r)[TPT], long n0, long end,
+                                            float (&x)[TPT][8]) {
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    Elem<E>::unpack(r[i], x[i]);
+    if (n0 + i >= end) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[i][c] = 0.f;
+    }
+  }
+}
+
+// Stage the RoPE rows of the frames a chunk spans (or use the global table).
+template <int D, bool LDSR>
+__device__ __forceinline__ typename Rope<D>::View rope_view(float2* lds, const float2* __restrict__ rope,
+                                                            const Geometry& G, long begin, long end) {
+  if constexpr (LDSR) {
+    const int HW = G.H * G.W;
+    const int t_lo = begin < end ? (int)(begin / HW) : 0;
+    const int nt = begin < end ? (int)((end - 1) / HW) - t_lo + 1 : 0;
+    return Rope<D>::template stage<kRopeLdsEntries>(lds, rope, G.T, G.H, G.W, t_lo, nt);
+  } else {
+    return typename Rope<D>::View{rope, 0, G.T, G.H};
+  }
+}
+
+}  // namespace gla

@@ -1,0 +1,52 @@
+// Launch sequence of one operator call: RoPE table, state partials,
+// reduce/prefix, fused output, each bracketed by the optional timer.
+#include "gla_launch.h"
+
+namespace gla {
+
+typedef unsigned short bf16_t;
+
+template <int D> hipError_t launch_rope_table(const LaunchArgs& a);
+template <int D> hipError_t launch_state_reduce(const LaunchArgs& a);
+template <int D, typename E> hipError_t launch_state_partial(const LaunchArgs& a);
+template <int D, typename E> hipError_t launch_output(const LaunchArgs& a);
+
+template <int D, typename E>
+static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
+  hipError_t e;
+  tm.begin(0, a.stream);
+  e = launch_rope_table<D>(a);
+  tm.end(0, a.stream);
+  if (e != hipSuccess) return e;
+  tm.begin(1, a.stream);
+  e = launch_state_partial<D, E>(a);
+  tm.end(1, a.stream);
+  if (e != hipSuccess) return e;
+  tm.begin(2, a.stream);
+  e = launch_state_reduce<D>(a);
+  tm.end(2, a.stream);
+  if (e != hipSuccess) return e;
+  tm.begin(3, a.stream);
+  e = launch_output<D, E>(a);
+  tm.end(3, a.stream);
+  return e;
+}
+
+hipError_t launch_operator(const LaunchArgs& a, Timer& tm) {
+  if (a.bf16) {
+    switch (a.geo.d) {
+      case 32: return launch_all<32, bf16_t>(a, tm);
+      case 64: return launch_all<64, bf16_t>(a, tm);
+      case 128: return launch_all<128, bf16_t>(a, tm);
+    }
+  } else {
+    switch (a.geo.d) {
+      case 32: return launch_all<32, float>(a, tm);
+      case 64: return launch_all<64, float>(a, tm);
+      case 128: return launch_all<128, float>(a, tm);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla

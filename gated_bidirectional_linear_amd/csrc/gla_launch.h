@@ -1,4 +1,25 @@
 // Internal interface between the C ABI (gla_abi.cpp) and the kernel launchers.
+//
+// The operator (SANA-Video 2.0 digest, prelims "gated bilinear linear
+// attention"; SANA-Video notes, key designs 1 and 2), per head, with
+// q^ = q/rms(q), k^ = k/rms(k), phi = ReLU, R_n the 3D RoPE rotation of token n:
+//   S = sum_n beta_n v_n (R_n phi k^_n)^T,   z = sum_n phi k^_n
+//   o_j = w * rmsnorm( sigmoid(g_j) * (S R_j phi q^_j) / (phi q^_j . z + eps) )
+//
+// The tokens are cut into "segments": one segment of N tokens for the
+// bidirectional form, or one per block of latent frames for the block-causal
+// form.  Four launches on the caller's stream:
+//   1. rope_table_kernel    (gla_tables.hip): per-axis cos/sin tables, fp64 angles.
+//   2. state_partial kernels (gla_state.hip): one workgroup per (head, chunk of
+//      a segment) builds the partial V^T (beta R phi K^) on MFMA with fp32
+//      accumulation, plus the partial key sum.
+//   3. state_reduce_kernel  (gla_tables.hip): fixed-shape pairwise tree over the
+//      chunk partials of each segment, then an inclusive prefix over segments
+//      on top of the carried state -> per-segment states.
+//   4. output_kernel        (gla_output.hip): one workgroup per (head, chunk of
+//      tiles) holds its slice of S as MFMA A-fragments, streams q and g,
+//      computes num^T = S RQ^T on MFMA, the denominator, gate and RMSNorm, and
+//      writes the output once.
 #pragma once
 #include <hip/hip_runtime_api.h>
 
@@ -23,6 +44,7 @@ struct Geometry {
   int chunk2;   // pass-2 tokens per chunk
   int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
   int rope_lds2;  // same for pass 2
+  int pass1_reg;  // pass 1 uses the fragment-built kernel (bf16, d = 128, tensors < 2 GiB)
   float eps;
 };
 

@@ -1,0 +1,90 @@
+// RoPE table generation and the fixed-order reduction / block prefix of the
+// per-chunk state partials.
+#include "gla_common.h"
+
+namespace gla {
+
+// ===========================================================================
+// 1. RoPE tables
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W) {
+  using R = Rope<D>;
+  const long total = (long)T * R::PT + (long)H * R::PY + (long)W * R::PX;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  long pos, i;
+  int da;
+  if (idx < (long)T * R::PT) {
+    pos = idx / R::PT; i = idx % R::PT; da = D / 4;
+  } else if (idx < (long)T * R::PT + (long)H * R::PY) {
+    const long r = idx - (long)T * R::PT;
+    pos = r / R::PY; i = r % R::PY; da = 3 * D / 8;
+  } else {
+    const long r = idx - (long)T * R::PT - (long)H * R::PY;
+    pos = r / R::PX; i = r % R::PX; da = 3 * D / 8;
+  }
+  const double ang = (double)pos * pow(10000.0, -2.0 * (double)i / (double)da);
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// ===========================================================================
+// 3. Reduce chunk partials per segment (pairwise tree of fixed shape), then
+//    inclusive prefix over segments on top of the carried state.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restrict__ partial,
+                                                           const float* S_in, const float* z_in,
+                                                           float* __restrict__ states, float* S_out,
+                                                           float* z_out, Geometry G) {
+  constexpr int SZ = D * D + D;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  if (e >= SZ) return;
+  float running = 0.f;
+  if (S_in != nullptr) running = (e < D * D) ? S_in[(size_t)h * D * D + e] : z_in[(size_t)h * D + (e - D * D)];
+  const float* src = partial + (size_t)h * G.nseg * G.cps1 * SZ + e;
+  for (int s = 0; s < G.nseg; ++s) {
+    float v[kMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
+#pragma unroll
+    for (int w = kMaxChunks / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) v[i] += v[i + w];
+    running += v[0];
+    states[((size_t)s * G.heads + h) * SZ + e] = running;
+  }
+  if (S_out != nullptr) {
+    if (e < D * D) S_out[(size_t)h * D * D + e] = running;
+    else z_out[(size_t)h * D + (e - D * D)] = running;
+  }
+}
+
+template <int D>
+hipError_t launch_rope_table(const LaunchArgs& a) {
+  const Geometry& G = a.geo;
+  const long total = (long)G.T * (D / 8) + (long)G.H * (3 * D / 16) + (long)G.W * (3 * D / 16);
+  const int blocks = (int)((total + 255) / 256);
+  hipLaunchKernelGGL((rope_table_kernel<D>), dim3(blocks), dim3(256), 0, a.stream, a.rope, G.T, G.H, G.W);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_state_reduce(const LaunchArgs& a) {
+  const Geometry& G = a.geo;
+  constexpr int SZ = D * D + D;
+  dim3 grid((SZ + 255) / 256, G.heads);
+  hipLaunchKernelGGL((state_reduce_kernel<D>), grid, dim3(256), 0, a.stream, (const float*)a.partial, a.S_in, a.z_in,
+                     a.states, a.S_out, a.z_out, G);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rope_table<32>(const LaunchArgs&);
+template hipError_t launch_rope_table<64>(const LaunchArgs&);
+template hipError_t launch_rope_table<128>(const LaunchArgs&);
+template hipError_t launch_state_reduce<32>(const LaunchArgs&);
+template hipError_t launch_state_reduce<64>(const LaunchArgs&);
+template hipError_t launch_state_reduce<128>(const LaunchArgs&);
+
+}  // namespace gla
