@@ -24,8 +24,10 @@ __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u &
 __device__ __forceinline__ uint16_t f2bf(float f) {   // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
-__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {   // one v_cvt_pk_bf16_f32
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, b2v));
 }
 
 // ---------------------------------------------------------------------------
@@ -57,6 +59,16 @@ template <> struct Elem<float> {
     __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p) + 1);
   }
   __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static Raw pack(const float (&x)[8]) {
+    Raw r;
+    r.a = (f32x4){x[0], x[1], x[2], x[3]};
+    r.b = (f32x4){x[4], x[5], x[6], x[7]};
+    return r;
+  }
+  __device__ __forceinline__ static void store_raw(float* p, const Raw& r) {
+    __builtin_nontemporal_store(r.a, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(r.b, reinterpret_cast<f32x4*>(p) + 1);
+  }
 };
 
 template <> struct Elem<bf16_t> {
@@ -80,6 +92,12 @@ template <> struct Elem<bf16_t> {
   }
   __device__ __forceinline__ static float load1(const bf16_t* p) {
     return __uint_as_float(((uint32_t)*p) << 16);
+  }
+  __device__ __forceinline__ static Raw pack(const float (&x)[8]) {
+    return (u32x4){pack2bf(x[0], x[1]), pack2bf(x[2], x[3]), pack2bf(x[4], x[5]), pack2bf(x[6], x[7])};
+  }
+  __device__ __forceinline__ static void store_raw(bf16_t* p, const Raw& r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
   }
 };
 
@@ -236,6 +254,91 @@ struct Rope {
       if (i < total) lds[i] = tmp[j];
     }
     return View{lds, t_lo, nt, H};
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Raw buffer access.  A buffer resource (gfx9 descriptor word 3 = 0x00020000,
+// stride 0) over `bytes` bytes from `p`: loads past the range return zero and
+// stores past it are dropped.  Offsets are a per-lane VGPR plus a
+// wave-uniform SGPR, so streaming loops need no per-lane 64-bit addresses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)voff, (int)soff, 0);
+}
+// 8 channels of one row: 16 bytes (bf16) or 32 bytes (fp32)
+template <typename E> struct BufRow;
+template <> struct BufRow<bf16_t> {
+  typedef u32x4 Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return buf_load16(r, voff, soff);
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const Raw& v) {
+    buf_store16(r, voff, soff, v);
+  }
+};
+template <> struct BufRow<float> {
+  typedef Elem<float>::Raw Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    Raw x;
+    x.a = __builtin_bit_cast(f32x4, buf_load16(r, voff, soff));
+    x.b = __builtin_bit_cast(f32x4, buf_load16(r, voff + 16, soff));
+    return x;
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const Raw& v) {
+    buf_store16(r, voff, soff, __builtin_bit_cast(u32x4, v.a));
+    buf_store16(r, voff + 16, soff, __builtin_bit_cast(u32x4, v.b));
+  }
+};
+
+// bf16 helpers working on packed pairs
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+// sum of squares of the two bf16 values in u, added to acc (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2sq(uint32_t u, float acc) {
+  const bf16x2 v = __builtin_bit_cast(bf16x2, u);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+// ReLU of both bf16 values: the sign bit of bf16 is the int16 sign bit, and
+// int16 order matches value order on the non-negative side (v_pk_max_i16)
+__device__ __forceinline__ uint32_t relu2(uint32_t u) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, u), (s16x2){0, 0}));
+}
+
+// Position (t, y, x) of a token on the latent grid, advanced without division.
+struct GridPos {
+  int t, y, x;
+  __device__ __forceinline__ void set(int n, int H, int W) {
+    const int HW = H * W;
+    t = n / HW;
+    const int rem = n - t * HW;
+    y = rem / W;
+    x = rem - y * W;
+  }
+  // n + (dt*H*W + dy*W + dx) with dx < W, dy < H
+  __device__ __forceinline__ void advance(int dt, int dy, int dx, int H, int W) {
+    x += dx;
+    const bool cy = x >= W;
+    x = cy ? x - W : x;
+    y += dy + (cy ? 1 : 0);
+    const bool ct = y >= H;
+    y = ct ? y - H : y;
+    t += dt + (ct ? 1 : 0);
+  }
+  __device__ __forceinline__ void next(int H, int W) {   // n + 1
+    ++x;
+    const bool cy = x == W;
+    x = cy ? 0 : x;
+    y += cy ? 1 : 0;
+    const bool ct = y == H;
+    y = ct ? 0 : y;
+    t += ct ? 1 : 0;
   }
 };
 

@@ -10,42 +10,70 @@ template <int D, typename E>
 struct OutputCfg {
   static constexpr int CG = D / 8;
   static constexpr int TG = kThreads / CG;
-  static constexpr int TPT = kTile / TG;
+  // 32-token tiles where every thread still has a whole token (d >= 64):
+  // half the LDS and prefetch registers of 64-token tiles, so more
+  // workgroups fit on a CU
+  static constexpr int TILE = TG > 32 ? TG : 32;
+  static constexpr int TPT = TILE / TG;
   static constexpr int MT = D / 32;                 // v-channel tiles
-  static constexpr int NTK = kTile / 32;            // token tiles
+  static constexpr int NTK = TILE / 32;             // token tiles
   static constexpr int PAIRS = MT * NTK;
   static constexpr int PPW = PAIRS >= 4 ? PAIRS / 4 : 1;   // (v tile, token tile) pairs per wave
   static constexpr int ACTIVE = PAIRS >= 4 ? 4 : PAIRS;    // waves with MFMA work
   static constexpr int RQ_PITCH = D + (Elem<E>::is_bf16 ? 8 : 4);  // elements
   static constexpr int NUM_PITCH = D + 4;                           // floats
-  static constexpr int RQ_BYTES = kTile * RQ_PITCH * (int)sizeof(E);
-  static constexpr int NUM_BYTES = kTile * NUM_PITCH * 4;
-  static constexpr int SMEM = RQ_BYTES > NUM_BYTES ? RQ_BYTES : NUM_BYTES;
+  static constexpr int RQ_BYTES = TILE * RQ_PITCH * (int)sizeof(E);
+  static constexpr int NUM_BYTES = TILE * NUM_PITCH * 4;
+  static constexpr int SMEM = RQ_BYTES + NUM_BYTES;   // separate regions: two barriers per tile
 };
 
+// The q-side RMS scale is folded out of the per-element work: with
+// r = sqrt(mean(q^2) + eps), phi(q/r) = phi(q)/r, so
+//   sigmoid(g) * S R phi(q^) / (phi(q^) . z + eps)
+//     = sigmoid(g) * S R phi(q) / (phi(q) . z + eps * r).
+// The MFMA therefore takes the rotated raw features, and the output RMSNorm
+// of x = y / den (y = sigmoid(g) * num) uses the per-token scale
+//   rden * rsqrt(rden^2 * mean(y^2) + eps),  rden = 1 / den.
 template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void output_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ rms_w, const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
   using C = OutputCfg<D, E>;
   using M = Mfma<E>;
+  using R = Rope<D>;
+  using BR = BufRow<E>;
+  typedef typename BR::Raw Raw;
   constexpr int KSTEPS = D / M::KSTEP;
   constexpr int SZ = D * D + D;
   constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
+  constexpr bool kBf16 = Elem<E>::is_bf16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
-  E* rqs = reinterpret_cast<E*>(smem);            // [kTile][RQ_PITCH]  (token, k channel)
-  float* nums = reinterpret_cast<float*>(smem);   // [kTile][NUM_PITCH] (token, v channel)
+  constexpr int kT = C::TILE;
+  E* rqs = reinterpret_cast<E*>(smem);                          // [kT][RQ_PITCH]  (token, k channel)
+  float* nums = reinterpret_cast<float*>(smem + C::RQ_BYTES);   // [kT][NUM_PITCH] (token, v channel)
 
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps2, G.chunk2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int cg = tid % C::CG;
   const int tg = tid / C::CG;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int HW = G.H * G.W;
+
+  // Buffer resources based at this chunk's first row and head, so offsets
+  // stay small whatever the tensor size; rows past the sequence read as zero.
+  const uint32_t ROW = (uint32_t)G.heads * D * sizeof(E);
+  const size_t base_off = (size_t)ch.begin * ROW + (size_t)ch.head * D * sizeof(E);
+  const uint64_t rest = (uint64_t)(G.N - ch.begin) * ROW - (uint64_t)ch.head * D * sizeof(E);
+  const uint32_t nrec = rest > 0xffffffffull ? 0xffffffffu : (uint32_t)rest;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const char*>(q) + base_off, nrec);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(reinterpret_cast<const char*>(g) + base_off, nrec);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(reinterpret_cast<const char*>(out) + base_off, nrec);
+  uint32_t voff[C::TPT];
+#pragma unroll
+  for (int i = 0; i < C::TPT; ++i) voff[i] = (uint32_t)(tg * C::TPT + i) * ROW + 8u * cg * sizeof(E);
 
   const float* Sst = states + ((size_t)ch.seg * G.heads + ch.head) * SZ;
   // This wave's v-channel tile of S as MFMA A-fragments: A[m = v ch][k = k ch].
@@ -68,116 +96,152 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
     wc[c] = rms_w[8 * cg + c];
   }
 
-  typename Elem<E>::Raw qr[C::TPT], gr[C::TPT];
-  auto issue = [&](long t0) {
-    const long n0 = t0 + (long)tg * C::TPT;
-    issue_rows<D, E, C::TPT>(q, n0, ch.end, G.heads, ch.head, cg, qr);
-    issue_rows<D, E, C::TPT>(g, n0, ch.end, G.heads, ch.head, cg, gr);
+  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  // RoPE rows of this thread's 4 pairs: one axis when they share it
+  const int p0 = 4 * cg;
+  const int axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
+  const int rbase = axis == 0 ? p0 - rv.t_lo * R::PT
+                  : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
+  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+  // grid position of this thread's first token, advanced by kT per tile
+  GridPos pos;
+  pos.set((int)min(ch.begin + (long)tg * C::TPT, (long)G.N - 1), G.H, G.W);
+  const int HW = G.H * G.W;
+  const int adt = kT / HW, ady = (kT % HW) / G.W, adx = kT % G.W;
+
+  // Two tiles of q/g rows in flight: buffers A and B alternate.
+  Raw qa[C::TPT], ga[C::TPT], qb[C::TPT], gb[C::TPT];
+  auto issue = [&](Raw (&qr)[C::TPT], Raw (&gr)[C::TPT], long t0) {
+    const uint32_t soff = (uint32_t)(t0 - ch.begin) * ROW;
+#pragma unroll
+    for (int i = 0; i < C::TPT; ++i) {
+      qr[i] = BR::load(qrs, voff[i], soff);
+      gr[i] = BR::load(grs, voff[i], soff);
+    }
   };
-  const typename Rope<D>::View rv =
-      rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
-  if (ch.begin < ch.end) issue(ch.begin);
+  if (ch.begin < ch.end) issue(qa, ga, ch.begin);
+  if (ch.begin + kT < ch.end) issue(qb, gb, ch.begin + kT);
   if constexpr (LDSR) lds_barrier();
 
-  for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
-    const long n0 = t0 + (long)tg * C::TPT;
-    float qx[C::TPT][8], gx[C::TPT][8];
-    float rden[C::TPT];
-    unpack_rows<E, C::TPT>(qr, n0, ch.end, qx);
-    unpack_rows<E, C::TPT>(gr, n0, ch.end, gx);
-    typename Rope<D>::CS cs[C::TPT];
+  auto tile = [&](Raw (&qr)[C::TPT], Raw (&gr)[C::TPT], long t0) {
+    const uint32_t soff = (uint32_t)(t0 - ch.begin) * ROW;
+    const uint32_t soff_next = (uint32_t)(t0 + 2 * kT - ch.begin) * ROW;
+    const bool refill = t0 + 2 * kT < ch.end;   // uniform
+    // RoPE entries of this tile's tokens
+    typename R::CS cs[C::TPT];
+    GridPos pp = pos;
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
-      const int n = (int)min(n0 + i, (long)G.N - 1);
-      const int t = n / HW;
-      const int rem = n - t * HW;
-      const int y = rem / G.W;
-      cs[i] = Rope<D>::fetch(rv, cg, t, y, rem - y * G.W);
+      if constexpr (R::kGrouped) {
+        const int ps = axis == 0 ? pp.t : (axis == 1 ? pp.y : pp.x);
+        const f32x4* e = reinterpret_cast<const f32x4*>(rv.tab + rbase + ps * rstride);
+        const f32x4 a = e[0], b = e[1];
+        cs[i].c[0] = a.x; cs[i].s[0] = a.y; cs[i].c[1] = a.z; cs[i].s[1] = a.w;
+        cs[i].c[2] = b.x; cs[i].s[2] = b.y; cs[i].c[3] = b.z; cs[i].s[3] = b.w;
+      } else {
+        cs[i] = R::fetch(rv, cg, pp.t, pp.y, pp.x);
+      }
+      pp.next(G.H, G.W);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (t0 + kTile < ch.end) issue(t0 + kTile);   // prefetch the next tile
-    __builtin_amdgcn_sched_barrier(0);
+    pos.advance(adt, ady, adx, G.H, G.W);
 
+    float rden[C::TPT];
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
+      float ph[8];
       float ss = 0.f;
+      if constexpr (kBf16) {
+        const u32x4 u = qr[i];
+        ss = dot2sq(u.x, ss); ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
+        const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
+        Elem<E>::unpack(rl, ph);
+      } else {
+        Elem<E>::unpack(qr[i], ph);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) ss += qx[i][c] * qx[i][c];
-      ss = group_sum<C::CG>(ss);
-      const float inv = rsqrtf(ss * (1.0f / D) + G.eps);
+        for (int c = 0; c < 8; ++c) {
+          ss += ph[c] * ph[c];
+          ph[c] = fmaxf(ph[c], 0.f);
+        }
+      }
       float dp = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float p = fmaxf(qx[i][c] * inv, 0.f);
-        qx[i][c] = p;
-        dp += p * zc[c];
-      }
+      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
+      ss = group_sum<C::CG>(ss);
       dp = group_sum<C::CG>(dp);
-      rden[i] = 1.0f / (dp + G.eps);
-      Rope<D>::apply(qx[i], cs[i]);
+      const float ms = ss * (1.0f / D) + G.eps;
+      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
+      rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * r);   // v_rcp_f32, 1 ulp
+      R::apply(ph, cs[i]);
       E* dst = rqs + (tg * C::TPT + i) * C::RQ_PITCH + 8 * cg;
-      if constexpr (Elem<E>::is_bf16) {
-        uint4 u;
-        u.x = pack2bf(qx[i][0], qx[i][1]); u.y = pack2bf(qx[i][2], qx[i][3]);
-        u.z = pack2bf(qx[i][4], qx[i][5]); u.w = pack2bf(qx[i][6], qx[i][7]);
-        *reinterpret_cast<uint4*>(dst) = u;
+      if constexpr (kBf16) {
+        *reinterpret_cast<u32x4*>(dst) = Elem<E>::pack(ph);
       } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(qx[i][0], qx[i][1], qx[i][2], qx[i][3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(qx[i][4], qx[i][5], qx[i][6], qx[i][7]);
+        *reinterpret_cast<f32x4*>(dst) = (f32x4){ph[0], ph[1], ph[2], ph[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){ph[4], ph[5], ph[6], ph[7]};
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) gx[i][c] = 1.0f / (1.0f + __expf(-gx[i][c]));
     }
+    // q rows consumed: refill with the rows two tiles ahead
+    if (refill) {
+#pragma unroll
+      for (int i = 0; i < C::TPT; ++i) qr[i] = BR::load(qrs, voff[i], soff_next);
+    }
+    // rq tile complete; every wave has also finished reading the previous
+    // tile's nums, so they may be overwritten below
     lds_barrier();
 
-    f32x16 acc[C::PPW];
     if (wave < C::ACTIVE) {
 #pragma unroll
       for (int u = 0; u < C::PPW; ++u) {
+        f32x16 acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
         const int ntt = (wave * C::PPW + u) % C::NTK;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const typename M::frag b = M::lds_frag(rqs + (32 * ntt + l32) * C::RQ_PITCH + ks * M::KSTEP + M::KPL * hi);
-          acc[u] = M::mma(sfrag[ks], b, acc[u]);
+          acc = M::mma(sfrag[ks], b, acc);
         }
-      }
-    }
-    lds_barrier();
-    if (wave < C::ACTIVE) {
-#pragma unroll
-      for (int u = 0; u < C::PPW; ++u) {
-        const int ntt = (wave * C::PPW + u) % C::NTK;
         float* row = nums + (32 * ntt + l32) * C::NUM_PITCH + 32 * dvt + 4 * hi;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          *reinterpret_cast<float4*>(row + 8 * rb) =
-              make_float4(acc[u][4 * rb], acc[u][4 * rb + 1], acc[u][4 * rb + 2], acc[u][4 * rb + 3]);
+          *reinterpret_cast<f32x4*>(row + 8 * rb) = (f32x4){acc[4 * rb], acc[4 * rb + 1], acc[4 * rb + 2], acc[4 * rb + 3]};
       }
     }
+    // nums complete; every wave has also finished reading rq
     lds_barrier();
 
+    const bool full = t0 + kT <= ch.end;   // uniform
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
       const float* src = nums + (tg * C::TPT + i) * C::NUM_PITCH + 8 * cg;
-      const float4 a = *reinterpret_cast<const float4*>(src);
-      const float4 b = *reinterpret_cast<const float4*>(src + 4);
-      float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      float gv[8];
+      Elem<E>::unpack(gr[i], gv);
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        x[c] = gx[i][c] * x[c] * rden[i];
-        ss += x[c] * x[c];
+        y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));   // sigmoid(g) * num
+        ss += y[c] * y[c];
       }
       ss = group_sum<C::CG>(ss);
-      const float inv = rsqrtf(ss * (1.0f / D) + G.eps);
+      const float rd = rden[i];
+      const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) x[c] = wc[c] * x[c] * inv;
-      const long n = n0 + i;
-      if (n < ch.end) Elem<E>::store8(out + ((size_t)n * G.heads + ch.head) * D + 8 * cg, x);
+      for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
+      if (full || t0 + tg * C::TPT + i < ch.end) BR::store(ors, voff[i], soff, Elem<E>::pack(y));
     }
-    lds_barrier();
+    // g rows consumed: refill with the rows two tiles ahead
+    if (refill) {
+#pragma unroll
+      for (int i = 0; i < C::TPT; ++i) gr[i] = BR::load(grs, voff[i], soff_next);
+    }
+  };
+
+  for (long t0 = ch.begin; t0 < ch.end; t0 += 2 * kT) {
+    tile(qa, ga, t0);
+    if (t0 + kT < ch.end) tile(qb, gb, t0 + kT);
   }
 }
 

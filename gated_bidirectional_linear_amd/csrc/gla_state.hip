@@ -324,6 +324,9 @@ __global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
     int yy = rem / G.W;
     int xx = rem - yy * G.W;
     const bool full = base + kStep <= ch.end;   // wave-uniform
+    // The k-side RMS scale rides on the per-token factor: with
+    // inv = 1/sqrt(mean(k^2) + eps), phi(k inv) = inv phi(k), so
+    // rk = (beta inv) R phi(k) and the key sum adds inv phi(k).
     uint32_t kp[4][4];   // [channel slot c][token pair]
 #pragma unroll
     for (int ip = 0; ip < 4; ++ip) {
@@ -331,26 +334,24 @@ __global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int i = 2 * ip + j;
-        const float kf[4] = {bf16lo(r.k[i].x), bf16hi(r.k[i].x), bf16lo(r.k[i].y), bf16hi(r.k[i].y)};
-        float ss = kf[0] * kf[0] + kf[1] * kf[1] + kf[2] * kf[2] + kf[3] * kf[3];
+        float ss = dot2sq(r.k[i].x, dot2sq(r.k[i].y, 0.f));
         ss = group_sum<16>(ss);
         ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));  // lane ^ 16
-        const float inv = rsqrtf(ss * (1.0f / D) + G.eps);
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + G.eps);
         // beta of token base + 8h + i lives in lane 8h + i
         const float bt = __int_as_float(__builtin_amdgcn_ds_bpermute((8 * h + i) * 4, bsrc));
-        const float keep = (full || n0 + i < ch.end) ? 1.f : 0.f;
-        float ph[4];
+        const float keep = (full || n0 + i < ch.end) ? inv : 0.f;
+        const uint32_t p01 = relu2(r.k[i].x), p23 = relu2(r.k[i].y);
+        const float ph[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          ph[c] = fmaxf(kf[c] * inv, 0.f) * keep;
-          zacc[c] += ph[c];
-        }
+        for (int c = 0; c < 4; ++c) zacc[c] += ph[c] * keep;
+        const float sc = bt * keep;
         const int pos = axis == 0 ? tt : (axis == 1 ? yy : xx);
         const f32x4 cs = *reinterpret_cast<const f32x4*>(rv.tab + rbase + pos * rstride);
-        rk2[j][0] = bt * (ph[0] * cs.x - ph[1] * cs.y);
-        rk2[j][1] = bt * (ph[0] * cs.y + ph[1] * cs.x);
-        rk2[j][2] = bt * (ph[2] * cs.z - ph[3] * cs.w);
-        rk2[j][3] = bt * (ph[2] * cs.w + ph[3] * cs.z);
+        rk2[j][0] = sc * (ph[0] * cs.x - ph[1] * cs.y);
+        rk2[j][1] = sc * (ph[0] * cs.y + ph[1] * cs.x);
+        rk2[j][2] = sc * (ph[2] * cs.z - ph[3] * cs.w);
+        rk2[j][3] = sc * (ph[2] * cs.w + ph[3] * cs.z);
         ++xx;
         const bool wy = xx == G.W;
         xx = wy ? 0 : xx;
