@@ -73,6 +73,84 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
+def _pmc_means(csv_path: str, counter: str) -> dict:
+    """Mean per-dispatch value of one counter, per kernel name, from a
+    rocprofv3 counter_collection.csv (values summed over dimensions)."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter:
+            per[(r["Dispatch_Id"], r["Kernel_Name"])] += float(r["Counter_Value"])
+    sums = collections.defaultdict(list)
+    for (d, k), v in per.items():
+        sums[k].append(v)
+    return {k: sum(v) / len(v) for k, v in sums.items()}
+
+
+def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, commands: str) -> None:
+    """Turn FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM bytes per
+    launch of the two streaming kernels, each counter scaled by what it reads
+    for a device-to-device copy of calib_mib MiB (read calib_mib, write calib_mib)."""
+    fetch = _pmc_means(fetch_csv, "FETCH_SIZE")
+    write = _pmc_means(write_csv, "WRITE_SIZE")
+    # the calibration copy is the only elementwise kernel in these runs
+    copy = [k for k in fetch if "elementwise" in k and "neg" in k.lower()] or \
+           [k for k in fetch if "elementwise" in k]
+    if not copy:
+        raise SystemExit("no calibration copy kernel in the counter runs (run bench.py with --calib-copy-mib)")
+    ck = max(copy, key=lambda k: fetch[k])
+    known_kib = calib_mib * 1024.0
+    f_scale = known_kib / fetch[ck]
+    w_scale = known_kib / write[ck]
+    for kernel in ("output_kernel", "state_partial"):
+        names = [k for k in fetch if kernel in k and k not in copy]
+        if not names:
+            continue
+        kn = names[0]
+        fetched = fetch[kn] * f_scale * 1024
+        written = write.get(kn, 0.0) * w_scale * 1024
+        short = "output_kernel" if kernel == "output_kernel" else "state_partial_kernel"
+        path = os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of {short} on the {workload} workload, from rocprofv3 counters\n")
+            f.write("# commands:\n")
+            for line in commands.strip().splitlines():
+                f.write(f"#   {line}\n")
+            f.write(f"kernel: {kn.split('(')[0]}\n")
+            f.write(f"FETCH_SIZE_kib_per_dispatch: {fetch[kn]:.1f}\n")
+            f.write(f"WRITE_SIZE_kib_per_dispatch: {write.get(kn, 0.0):.1f}\n")
+            f.write(f"copy_calibration: {ck.split('(')[0]} of {calib_mib} MiB read + {calib_mib} MiB written; "
+                    f"FETCH_SIZE {fetch[ck]:.1f} KiB, WRITE_SIZE {write[ck]:.1f} KiB\n")
+            f.write(f"fetch_scale: {f_scale:.4f}\n")
+            f.write(f"write_scale: {w_scale:.4f}\n")
+            f.write(f"read_bytes_per_launch: {fetched:.0f}\n")
+            f.write(f"write_bytes_per_launch: {written:.0f}\n")
+            f.write(f"traffic_bytes_per_launch: {fetched + written:.0f}\n")
+            f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+        print(f"wrote {path}: {(fetched + written) / 1e9:.3f} GB per launch")
+
+
+def write_stats_summary(stats_csv: str, workload: str, commands: str) -> None:
+    """Kernel-trace statistics (rocprofv3 --kernel-trace --stats, kernel_stats.csv)
+    as a short text table under profiles/."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}_stats.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace statistics, {workload} workload\n")
+        f.write("# commands:\n")
+        for line in commands.strip().splitlines():
+            f.write(f"#   {line}\n")
+        f.write(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}\n")
+        for r in rows:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            f.write(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                    f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+    print(f"wrote {path}")
+
+
 def cpu_baseline(w, inp, heads_sample: int):
     """Time the fp64 oracle on `heads_sample` heads of the full workload (all
     tokens, complete state and output) and scale to the whole workload."""
@@ -110,7 +188,25 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run 3 elementwise copies (torch.neg, fp32) reading and "
+                         "writing this many MiB: a streaming kernel of known size for counter calibration")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: write the traffic summaries under profiles/ from two rocprofv3 "
+                         "counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run)")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="CPU only: write the kernel-trace summary under profiles/ from a rocprofv3 "
+                         "kernel_stats.csv")
+    ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
     args = ap.parse_args(argv)
+
+    if args.stats_summary:
+        write_stats_summary(args.stats_summary, args.workload, args.pmc_commands)
+        return 0
+    if args.pmc_summary:
+        write_traffic_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024,
+                              args.workload, args.pmc_commands)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this operator's path is measured per GPU "
@@ -179,6 +275,15 @@ def main(argv=None):
     traffic = read_traffic(dom, w.name)
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
+
+    if args.calib_copy_mib > 0:
+        # an elementwise streaming kernel of known size: read and write calib MiB
+        src = torch.ones((args.calib_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

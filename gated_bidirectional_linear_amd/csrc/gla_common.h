@@ -14,11 +14,14 @@ struct Chunk {
   int head, seg, index;
 };
 
+// Chunk-major order: consecutive workgroup ids take the same chunk of
+// consecutive heads, so (after the XCD swizzle) all heads of a token range run
+// on one XCD at the same time: their rows share DRAM pages and the beta rows
+// (one cache line holds every head of a token) are fetched into one L2.
 __device__ __forceinline__ Chunk chunk_of(int lin, const Geometry& G, int cps, int chunk_len) {
   Chunk c;
-  const int per_head = G.nseg * cps;
-  c.head = lin / per_head;
-  const int ci = lin - c.head * per_head;
+  const int ci = lin / G.heads;          // chunk index within a head, over all segments
+  c.head = lin - ci * G.heads;
   c.seg = ci / cps;
   c.index = ci;
   const int j = ci - c.seg * cps;
