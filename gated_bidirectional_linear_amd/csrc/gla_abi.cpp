@@ -20,8 +20,8 @@ constexpr int kTile = 64;
 // workgroup, so it stays near two per CU (256 CUs); pass 2 has no such cost
 // and takes more for load balance.  Overridable for tuning sweeps.
 constexpr int kDefaultTargetWg1 = 512;
-// The fragment-built pass-1 kernel (bf16, d = 128) runs two workgroups per CU.
-constexpr int kDefaultTargetWgReg1 = 512;
+// The fragment-built pass-1 kernel (bf16, d = 128) runs three workgroups per CU.
+constexpr int kDefaultTargetWgReg1 = 768;
 constexpr int kDefaultTargetWg2 = 2048;
 
 int env_int(const char* name, int dflt) {

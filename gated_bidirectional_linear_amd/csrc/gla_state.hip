@@ -228,9 +228,9 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
 // packs channel c of the lane's 8 tokens with v_cvt_pk_bf16_f32, the v-side
 // fragment selects the same 16-bit halves from the raw rows with v_perm_b32.
 // The 8 fragments of each step go to LDS in lane order (16-byte, conflict-free
-// writes); after one barrier per tile, wave w accumulates the 4 output tiles
-// S[4m + w][4n + c] over the tile's 4 steps (16 MFMAs).  LDS is double
-// buffered, so one barrier per tile suffices.  Rows are read with raw buffer
+// writes); after a barrier, wave w accumulates the 4 output tiles
+// S[4m + w][4n + c] over the tile's 4 steps (16 MFMAs).  One fragment buffer
+// (two barriers per tile) keeps LDS at 48 KB for three workgroups per CU.  Rows are read with raw buffer
 // loads (wave-uniform token offset + one per-lane offset; tensors below
 // 2 GiB, checked by the host); rows past the sequence read as zero, rows past
 // the chunk are masked.
@@ -265,14 +265,14 @@ __device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 }  // namespace frag1
 
 template <bool LDSR>
-__global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void state_partial_frag_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ beta,
     const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   constexpr int D = 128;
   using namespace frag1;
   using R = Rope<D>;
   constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes + ROPE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTileBytes + ROPE_BYTES];
 
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps1, G.chunk1);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
 
   // this lane's RoPE axis (pairs 2m and 2m+1 share it)
   const int axis = (2 * m < R::PT) ? 0 : ((2 * m < R::PT + R::PY) ? 1 : 2);
-  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + 2 * kTileBytes), rope, G,
+  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + kTileBytes), rope, G,
                                                  ch.begin, ch.end);
   const int rbase = axis == 0 ? 2 * m - rv.t_lo * R::PT
                   : (axis == 1 ? rv.nt * R::PT + (2 * m - R::PT) : rv.nt * R::PT + rv.H * R::PY + (2 * m - R::PT - R::PY));
@@ -383,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
 
   if constexpr (LDSR) lds_barrier();   // RoPE rows staged
   Rows rows;
-  int buf = 0;
   if (ch.begin < ch.end) issue(rows, ch.begin + wave * kStep);
   for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
-    unsigned char* tile = smem + buf * kTileBytes;
+    unsigned char* tile = smem;
+    if (t0 != ch.begin) lds_barrier();   // every wave is done with the previous tile's fragments
     const long base = t0 + wave * kStep;
     if (base < ch.end) {
       const Rows cur = rows;
@@ -410,7 +410,6 @@ __global__ __launch_bounds__(kThreads) void state_partial_frag_kernel(
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
       }
     }
-    buf ^= 1;
   }
 
   // key sums: lanes m and m + 32 hold the same channels; then across waves
