@@ -2,6 +2,7 @@
 // scratch, launch sequencing and optional per-kernel event timing.
 #include <hip/hip_runtime_api.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -20,8 +21,9 @@ constexpr int kTile = 64;
 // workgroup, so it stays near two per CU (256 CUs); pass 2 has no such cost
 // and takes more for load balance.  Overridable for tuning sweeps.
 constexpr int kDefaultTargetWg1 = 512;
-// The fragment-built pass-1 kernel (bf16, d = 128) runs three workgroups per CU.
-constexpr int kDefaultTargetWgReg1 = 768;
+// The bf16, d = 128 pass-1 kernel keeps whole states in registers and runs
+// one workgroup per CU.
+constexpr int kDefaultTargetWgAcc1 = 256;
 constexpr int kDefaultTargetWg2 = 2048;
 
 int env_int(const char* name, int dflt) {
@@ -53,10 +55,8 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
     return yx + frames * (d / 8) <= gla::kRopeLdsEntries;
   };
 
-  // buffer-load offsets of the fragment-built kernel are 32-bit
-  const bool small = (long long)T * H * W * heads * d * 2 < (1LL << 31);
-  G.pass1_reg = (bf16 && d == 128 && small && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
-  const int target1 = G.pass1_reg ? kDefaultTargetWgReg1 : kDefaultTargetWg1;
+  G.pass1_reg = (bf16 && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
+  const int target1 = G.pass1_reg ? kDefaultTargetWgAcc1 : kDefaultTargetWg1;
   const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
@@ -76,6 +76,8 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
+  // the register-accumulating kernel reads its RoPE rows from LDS only
+  if (!G.rope_lds1) G.pass1_reg = 0;
   return G;
 }
 
@@ -157,7 +159,7 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16) return GLA_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return GLA_ERR_UNSUPPORTED_D;
   if (T < 0 || H < 0 || W < 0 || heads < 1) return GLA_ERR_SHAPE;
-  if (!(std::isfinite(eps) && eps > 0.0f)) return GLA_ERR_SHAPE;
+  if (!(std::isfinite(eps) && eps >= FLT_MIN)) return GLA_ERR_SHAPE;
   if (causal && block_frames < 1) return GLA_ERR_SHAPE;
   const long long N = (long long)T * H * W;
   if (N >= (1LL << 31)) return GLA_ERR_SHAPE;

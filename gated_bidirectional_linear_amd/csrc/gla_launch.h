@@ -44,7 +44,7 @@ struct Geometry {
   int chunk2;   // pass-2 tokens per chunk
   int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
   int rope_lds2;  // same for pass 2
-  int pass1_reg;  // pass 1 uses the fragment-built kernel (bf16, d = 128, tensors < 2 GiB)
+  int pass1_reg;  // pass 1 uses the register-accumulating kernel (bf16, d = 128, RoPE rows in LDS)
   float eps;
 };
 

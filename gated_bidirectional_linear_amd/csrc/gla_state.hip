@@ -216,35 +216,108 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
 
 
 // ===========================================================================
-// Fragment-built pass 1 (bf16, d = 128).
+// Pass 1 for bf16, d = 128: MFMA operand fragments built in registers.
 //
-// A workgroup of 4 waves walks its chunk in 64-token tiles; wave w loads and
-// prepares the 16-token step w of every tile.  Lane l of a wave owns channels
-// 4m..4m+3 (m = l % 32) of 8 tokens; lanes 0-31 and 32-63 (h = l / 32) take
-// the two halves of the step.  Every row load is 8 bytes per lane and 32 lanes
-// cover a whole 256-byte token row (two full rows per load instruction).
-// Channel 4m + c is row/column m of MFMA tile c, so the 32x32x16 MFMA
-// operand fragments are built in registers: the k-side fragment of tile c
-// packs channel c of the lane's 8 tokens with v_cvt_pk_bf16_f32, the v-side
-// fragment selects the same 16-bit halves from the raw rows with v_perm_b32.
-// The 8 fragments of each step go to LDS in lane order (16-byte, conflict-free
-// writes); after a barrier, wave w accumulates the 4 output tiles
-// S[4m + w][4n + c] over the tile's 4 steps (16 MFMAs).  One fragment buffer
-// (two barriers per tile) keeps LDS at 48 KB for three workgroups per CU.  Rows are read with raw buffer
-// loads (wave-uniform token offset + one per-lane offset; tensors below
-// 2 GiB, checked by the host); rows past the sequence read as zero, rows past
-// the chunk are masked.
+// A wave works in 16-token steps.  Lane l owns channels 4m..4m+3 (m = l % 32)
+// of 8 tokens; lanes 0-31 and 32-63 (h = l / 32) take the two halves of the
+// step.  Every row load is 8 bytes per lane and 32 lanes cover a whole
+// 256-byte token row (two full rows per load instruction).  Channel 4m + c is
+// row/column m of MFMA slot c, so the 32x32x16 operand fragments come straight
+// from registers: the k-side fragment of slot c packs channel c of the lane's
+// 8 tokens with v_cvt_pk_bf16_f32, the v-side fragment selects the same 16-bit
+// halves of the raw rows with v_perm_b32.  Output tile (a, c) of the state is
+// S[4i + a][4j + c] (i, j = 0..31), the product of v-side slot a and k-side
+// slot c.
+//
+// Per-step work is kept off the vector ALU where it can be:
+//  * each step's loads go through buffer resources that end at the chunk's
+//    last row, so rows past it read as zero (k = 0, v = 0, beta = 0) and add
+//    nothing: no per-token masks;
+//  * lane l walks the grid position of its own token 8h + (l % 8) of the step
+//    and packs the three RoPE table row offsets of that token into one word;
+//    DPP row broadcasts hand a token's word and beta to the lanes of its half,
+//    which keep the table field of their own axis;
+//  * the RMS sum over a token's 32 lanes uses DPP within 16-lane rows and
+//    v_permlane16_swap across the two rows: no LDS round trips;
+//  * the LDS RoPE table holds, per pair, the bf16 words (cos, -sin) and
+//    (sin, cos), so each rotated channel is one v_dot2_f32_bf16 of the ReLU'd
+//    bf16 pair with fp32 accumulation;
+//  * the key sum takes two tokens per v_dot2_f32_bf16: (phi k_a, phi k_b) of
+//    one channel against their RMS factors (bf16).
+//
+// state_partial_acc_kernel: every wave keeps the whole 128 x 128 state of its
+// tokens in accumulation registers (16 tiles, 256 registers; one wave per
+// SIMD, one workgroup per CU) and runs the 16 MFMAs of each step on its own
+// fragments, 4 at a time between the token pairs of the next step (a wave
+// issues in order).  No LDS traffic or barriers in the loop; rows are fetched
+// three steps ahead.  The four waves' states are summed through LDS at the
+// end.
 // ===========================================================================
 namespace frag1 {
+constexpr int D = 128;
 constexpr int kStep = 16;    // tokens per step (one MFMA K)
-constexpr int kFragBytes = 64 * 16;            // one fragment for a wave
-constexpr int kStepBytes = 8 * kFragBytes;     // 4 k-side + 4 v-side fragments
-constexpr int kTileBytes = 4 * kStepBytes;     // the 4 steps of a tile
+constexpr int kOffBits = 10;                   // packed table row offset (16-byte units)
+constexpr int kRotBytes = kRopeLdsEntries * 8; // LDS rotation table
+using R = Rope<D>;
 
 struct Rows {
   u32x2 k[8], v[8];
-  uint32_t b;               // beta (bf16 bits) of token base + (lane & 15)
+  uint32_t b;               // beta (bf16 bits) of this lane's own token
 };
+
+// Per-lane constants of a chunk.
+struct Lane {
+  int lane, m, h;
+  uint32_t lane_off;        // byte offset of this lane's 8 bytes in a step's row 8h
+  uint32_t beta_off;        // byte offset of beta of this lane's own token in a step
+  uint32_t ROW;             // bytes between tokens
+  uint32_t lane_rel;        // this lane's pair offset inside a table row (16-byte units)
+  uint32_t ashift;          // bit offset of this lane's axis in the packed row offsets
+  int t_lo, t_last, nt;     // frames the chunk spans
+};
+
+__device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
+  Lane L;
+  L.lane = threadIdx.x & 63;
+  L.m = L.lane & 31;
+  L.h = L.lane >> 5;
+  L.ROW = (uint32_t)G.heads * D * 2;
+  L.lane_off = (uint32_t)(8 * L.h) * L.ROW + (uint32_t)ch.head * D * 2 + 8u * L.m;
+  L.beta_off = ((uint32_t)(8 * L.h + (L.lane & 7)) * (uint32_t)G.heads + (uint32_t)ch.head) * 2;
+  // pairs 2m and 2m+1 share an axis
+  const int axis = (2 * L.m < R::PT) ? 0 : ((2 * L.m < R::PT + R::PY) ? 1 : 2);
+  const int first = axis == 0 ? 0 : (axis == 1 ? R::PT : R::PT + R::PY);
+  L.lane_rel = (uint32_t)(2 * L.m - first) / 2;
+  L.ashift = (uint32_t)axis * kOffBits;
+  const int HW = G.H * G.W;
+  L.t_lo = ch.begin < ch.end ? (int)(ch.begin / HW) : 0;
+  L.t_last = ch.begin < ch.end ? (int)((ch.end - 1) / HW) : 0;
+  L.nt = L.t_last - L.t_lo + 1;
+  return L;
+}
+
+// RoPE rows of the frames the chunk spans, the y block and the x block, as
+// per-pair bf16 words (cos, -sin), (sin, cos).  All threads take part; the
+// caller synchronises.
+__device__ __forceinline__ void stage_rotations(unsigned char* rtab, const float2* __restrict__ rope,
+                                                const Geometry& G, const Lane& L) {
+  constexpr int PER = kRopeLdsEntries / kThreads;
+  const int n_t = L.nt * R::PT;
+  const int total = n_t + G.H * R::PY + G.W * R::PX;
+  float2 tmp[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    const int src = (i < n_t) ? L.t_lo * R::PT + i : G.T * R::PT + (i - n_t);
+    tmp[j] = rope[i < total ? src : 0];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (int)threadIdx.x + j * kThreads;
+    if (i < total)
+      *reinterpret_cast<u32x2*>(rtab + 8 * i) = (u32x2){pack2bf(tmp[j].x, -tmp[j].y), pack2bf(tmp[j].y, tmp[j].x)};
+  }
+}
 
 // bf16 pair (lo: token a, hi: token b) of channel c from two raw 4-channel rows
 __device__ __forceinline__ uint32_t sel_channel(u32x2 ra, u32x2 rb, int c) {
@@ -254,186 +327,260 @@ __device__ __forceinline__ uint32_t sel_channel(u32x2 ra, u32x2 rb, int c) {
   return (c & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
 }
 
-// Raw buffer resource over a whole tensor (gfx9 descriptor word 3): loads at
-// offsets past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+// Streaming loads carry the nontemporal hint (bit 1 of the cache-policy
+// operand): every row is read once.
+constexpr int kStreamPolicy = 2;
+__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kStreamPolicy));
 }
-__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+
+// sum of the two bf16 products a.lo*b.lo + a.hi*b.hi, accumulated in fp32
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// Rows [base, base + 16) of a step; rows at or past `end` read as zero.
+__device__ __forceinline__ void issue(Rows& r, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                      const bf16_t* __restrict__ beta, long base, long end, int heads,
+                                      const Lane& L) {
+  const long left = end - base;
+  const uint32_t nvalid = left <= 0 ? 0u : (left >= kStep ? (uint32_t)kStep : (uint32_t)left);
+  const size_t row0 = (size_t)base * heads * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + row0, nvalid * L.ROW);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + row0, nvalid * L.ROW);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + (size_t)base * heads, nvalid * (uint32_t)heads * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    r.k[i] = ld8(krs, L.lane_off + (uint32_t)i * L.ROW);
+    r.v[i] = ld8(vrs, L.lane_off + (uint32_t)i * L.ROW);
+  }
+  r.b = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, (int)L.beta_off, 0, 0);
+}
+
+// Table row offsets (16-byte units) of the token at `gp` on the three axes.
+__device__ __forceinline__ uint32_t table_rows(const GridPos& gp, const Lane& L, int H) {
+  const int tc = gp.t < L.t_last ? gp.t : L.t_last;
+  return (uint32_t)((tc - L.t_lo) * R::PT / 2) |
+         ((uint32_t)((L.nt * R::PT + gp.y * R::PY) / 2) << kOffBits) |
+         ((uint32_t)((L.nt * R::PT + H * R::PY + gp.x * R::PX) / 2) << (2 * kOffBits));
+}
+
+// Lane l "owns" token 8h + (l & 7) of a step: every 16-lane row holds the 8
+// tokens of its half, so DPP row_newbcast:i hands token i of the lane's half
+// to all lanes of a row without going through LDS.
+__device__ __forceinline__ int own_token(int lane) { return 8 * (lane >> 5) + (lane & 7); }
+template <int I>
+__device__ __forceinline__ int row_bcast(int x) {
+  return __builtin_amdgcn_mov_dpp(x, 0x150 + I, 0xF, 0xF, false);
+}
+// x[l] + x[l ^ 16]: v_permlane16_swap hands each lane both rows of its pair
+__device__ __forceinline__ float pair_rows_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// The 8 operand fragments of a step: kf[c] (k side) and vf[c] (v side).
+// `offs` holds the packed table rows of this lane's own token.  The k-side
+// RMS scale rides on the per-token factor: with
+// inv = 1/sqrt(mean(k^2) + eps), phi(k inv) = inv phi(k), so
+// rk = (beta inv) R phi(k) and the key sum adds inv phi(k).
+// `between(ip)` runs after token pair ip (0..3): a caller can put work of its
+// own (the previous step's MFMAs) between the vector instructions.
+struct NoWork {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+template <typename Between = NoWork>
+__device__ __forceinline__ void build_step(const Rows& r, uint32_t offs, const unsigned char* rtab, const Lane& L,
+                                           float eps, float (&zacc)[4], u32x4 (&kf)[4], u32x4 (&vf)[4],
+                                           Between between = Between()) {
+  const int bsrc = (int)(r.b << 16);
+  // rotation words of the 8 tokens: all table reads issued together
+  u32x4 cs[8];
+  float bt[8];
+#define GLA_FETCH(I)                                                                                 \
+  {                                                                                                  \
+    const uint32_t o = (uint32_t)row_bcast<I>((int)offs);                                            \
+    cs[I] = *reinterpret_cast<const u32x4*>(rtab + 16 * (__builtin_amdgcn_ubfe(o, L.ashift, kOffBits) + L.lane_rel)); \
+    bt[I] = __int_as_float(row_bcast<I>(bsrc));                                                      \
+  }
+  GLA_FETCH(0) GLA_FETCH(1) GLA_FETCH(2) GLA_FETCH(3) GLA_FETCH(4) GLA_FETCH(5) GLA_FETCH(6) GLA_FETCH(7)
+#undef GLA_FETCH
+  // RMS factors: 4 channels per lane, 16 lanes per row, two rows per token
+  float inv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float ss = dot2bf(r.k[i].x, r.k[i].x, dot2bf(r.k[i].y, r.k[i].y, 0.f));
+    ss = pair_rows_sum(group_sum<16>(ss));
+    inv[i] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  }
+  uint32_t kp[4][4];   // [channel slot c][token pair]
+#pragma unroll
+  for (int ip = 0; ip < 4; ++ip) {
+    float rk2[2][4];
+    uint32_t ph2[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = 2 * ip + j;
+      const float sc = bt[i] * inv[i];
+      const uint32_t p01 = relu2(r.k[i].x), p23 = relu2(r.k[i].y);
+      rk2[j][0] = sc * dot2bf(p01, cs[i].x, 0.f);
+      rk2[j][1] = sc * dot2bf(p01, cs[i].y, 0.f);
+      rk2[j][2] = sc * dot2bf(p23, cs[i].z, 0.f);
+      rk2[j][3] = sc * dot2bf(p23, cs[i].w, 0.f);
+      ph2[j][0] = p01;
+      ph2[j][1] = p23;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kp[c][ip] = pack2bf(rk2[0][c], rk2[1][c]);
+    // key sum: channel c of the token pair against (inv_a, inv_b)
+    const uint32_t ip2 = pack2bf(inv[2 * ip], inv[2 * ip + 1]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t pa = ph2[0][c >> 1], pb = ph2[1][c >> 1];
+      const uint32_t pr = (c & 1) ? __builtin_amdgcn_perm(pb, pa, 0x07060302u) : __builtin_amdgcn_perm(pb, pa, 0x05040100u);
+      zacc[c] = dot2bf(pr, ip2, zacc[c]);
+    }
+    between(ip);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    kf[c] = (u32x4){kp[c][0], kp[c][1], kp[c][2], kp[c][3]};
+    vf[c] = (u32x4){sel_channel(r.v[0], r.v[1], c), sel_channel(r.v[2], r.v[3], c),
+                    sel_channel(r.v[4], r.v[5], c), sel_channel(r.v[6], r.v[7], c)};
+  }
+}
+
+// Key sums of a workgroup: lanes m and m + 32 hold the same channels, then
+// across the 4 waves through `zred` (LDS, 2 KB); wave 0 writes them.
+__device__ __forceinline__ void write_key_sum(float (&zacc)[4], float* zred, float* dst, const Lane& L, int wave) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    zacc[c] += __int_as_float(__builtin_amdgcn_ds_bpermute((L.lane ^ 32) * 4, __float_as_int(zacc[c])));
+  if (L.h == 0) *reinterpret_cast<f32x4*>(zred + wave * 128 + 4 * L.m) = (f32x4){zacc[0], zacc[1], zacc[2], zacc[3]};
+  lds_barrier();
+  if (wave == 0 && L.lane < 32) {
+    f32x4 zz = *reinterpret_cast<const f32x4*>(zred + 4 * L.m);
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(zred + wv * 128 + 4 * L.m);
+      zz.x += o.x; zz.y += o.y; zz.z += o.z; zz.w += o.w;
+    }
+    *reinterpret_cast<f32x4*>(dst + D * D + 4 * L.m) = zz;
+  }
 }
 }  // namespace frag1
 
-template <bool LDSR>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void state_partial_frag_kernel(
+namespace acc1 {
+constexpr int kHalfBytes = 32 * 1024;        // half of one wave's state (v-side slots 2R, 2R + 1)
+constexpr int kSumBytes = 4 * kHalfBytes;    // the 4 waves' halves during the final sum
+#ifndef GLA_ACC_DEPTH
+#define GLA_ACC_DEPTH 3
+#endif
+constexpr int kDepth = GLA_ACC_DEPTH;        // steps of rows in flight per wave
+}  // namespace acc1
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_partial_acc_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ beta,
     const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
-  constexpr int D = 128;
   using namespace frag1;
-  using R = Rope<D>;
-  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kTileBytes + ROPE_BYTES];
+  using namespace acc1;
+  // the RoPE table and the final sum share LDS (the table is dead by then)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSumBytes + 2048];
+  unsigned char* const rtab = smem;
+  float* const zred = reinterpret_cast<float*>(smem + kSumBytes);
 
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps1, G.chunk1);
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int m = lane & 31;
-  const int h = lane >> 5;
+  const Lane L = make_lane(G, ch);
   const int HW = G.H * G.W;
-  const uint32_t ROW = (uint32_t)G.heads * D * 2;          // bytes between tokens
-  const __amdgpu_buffer_rsrc_t krs = tensor_rsrc(k, (uint32_t)G.N * ROW);
-  const __amdgpu_buffer_rsrc_t vrs = tensor_rsrc(v, (uint32_t)G.N * ROW);
-  const __amdgpu_buffer_rsrc_t brs = tensor_rsrc(beta, (uint32_t)G.N * G.heads * 2);
-  const uint32_t lane_off = (uint32_t)(8 * h) * ROW + (uint32_t)ch.head * D * 2 + 8u * m;
-  const uint32_t beta_off = ((uint32_t)(lane & 15) * (uint32_t)G.heads + (uint32_t)ch.head) * 2;
+  stage_rotations(rtab, rope, G, L);
 
-  // this lane's RoPE axis (pairs 2m and 2m+1 share it)
-  const int axis = (2 * m < R::PT) ? 0 : ((2 * m < R::PT + R::PY) ? 1 : 2);
-  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + kTileBytes), rope, G,
-                                                 ch.begin, ch.end);
-  const int rbase = axis == 0 ? 2 * m - rv.t_lo * R::PT
-                  : (axis == 1 ? rv.nt * R::PT + (2 * m - R::PT) : rv.nt * R::PT + rv.H * R::PY + (2 * m - R::PT - R::PY));
-  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+  // grid position of this lane's own token; a wave's steps are 64 apart
+  GridPos gp;
+  gp.set((int)(ch.begin + wave * kStep + own_token(L.lane)), G.H, G.W);
+  const int adt = kTile / HW, ady = (kTile % HW) / G.W, adx = (kTile % HW) % G.W;
 
-  f32x16 acc[4];
+  f32x16 acc[4][4];   // [v-side slot a][k-side slot c]
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
   float zacc[4] = {0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](Rows& r, long base) {
-    const uint32_t b = (uint32_t)base;
+  lds_barrier();   // RoPE rows staged
+
+  // The MFMAs of a step run while the next step is built: one wave per SIMD
+  // issues in order, so the 16 MFMAs of step s go out 4 at a time between
+  // the token pairs of step s + 1 (fragments pk, pv; zero before the first).
+  u32x4 pk[4], pv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      r.k[i] = ld8(krs, lane_off, (b + i) * ROW);
-      r.v[i] = ld8(vrs, lane_off, (b + i) * ROW);
-    }
-    r.b = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, (int)beta_off, (int)(b * (uint32_t)G.heads * 2), 0);
+  for (int c = 0; c < 4; ++c) pk[c] = pv[c] = (u32x4){0u, 0u, 0u, 0u};
+  auto mfma_row = [&](int a) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pv[a]),
+                                                          __builtin_bit_cast(bf16x8, pk[c]), acc[a][c], 0, 0, 0);
   };
 
-  // Build this lane's 8 fragments of the step starting at `base` and store
-  // them to LDS at `dst` (lane order).
-  auto prepare = [&](const Rows& r, long base, unsigned char* dst) {
-    const long n0 = base + 8 * h;
-    const int bsrc = (int)(r.b << 16);
-    const int nc = (int)min(n0, (long)G.N - 1);
-    int tt = nc / HW;
-    const int rem = nc - tt * HW;
-    int yy = rem / G.W;
-    int xx = rem - yy * G.W;
-    const bool full = base + kStep <= ch.end;   // wave-uniform
-    // The k-side RMS scale rides on the per-token factor: with
-    // inv = 1/sqrt(mean(k^2) + eps), phi(k inv) = inv phi(k), so
-    // rk = (beta inv) R phi(k) and the key sum adds inv phi(k).
-    uint32_t kp[4][4];   // [channel slot c][token pair]
-#pragma unroll
-    for (int ip = 0; ip < 4; ++ip) {
-      float rk2[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = 2 * ip + j;
-        float ss = dot2sq(r.k[i].x, dot2sq(r.k[i].y, 0.f));
-        ss = group_sum<16>(ss);
-        ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));  // lane ^ 16
-        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + G.eps);
-        // beta of token base + 8h + i lives in lane 8h + i
-        const float bt = __int_as_float(__builtin_amdgcn_ds_bpermute((8 * h + i) * 4, bsrc));
-        const float keep = (full || n0 + i < ch.end) ? inv : 0.f;
-        const uint32_t p01 = relu2(r.k[i].x), p23 = relu2(r.k[i].y);
-        const float ph[4] = {bf16lo(p01), bf16hi(p01), bf16lo(p23), bf16hi(p23)};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) zacc[c] += ph[c] * keep;
-        const float sc = bt * keep;
-        const int pos = axis == 0 ? tt : (axis == 1 ? yy : xx);
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(rv.tab + rbase + pos * rstride);
-        rk2[j][0] = sc * (ph[0] * cs.x - ph[1] * cs.y);
-        rk2[j][1] = sc * (ph[0] * cs.y + ph[1] * cs.x);
-        rk2[j][2] = sc * (ph[2] * cs.z - ph[3] * cs.w);
-        rk2[j][3] = sc * (ph[2] * cs.w + ph[3] * cs.z);
-        ++xx;
-        const bool wy = xx == G.W;
-        xx = wy ? 0 : xx;
-        yy += wy ? 1 : 0;
-        const bool wt = yy == G.H;
-        yy = wt ? 0 : yy;
-        tt += wt ? 1 : 0;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kp[c][ip] = pack2bf(rk2[0][c], rk2[1][c]);
-    }
-    // v rows past the chunk are zeroed so they cannot reach the state
-    uint32_t vmask[4];
-#pragma unroll
-    for (int ip = 0; ip < 4; ++ip) {
-      const bool v0 = full || n0 + 2 * ip < ch.end;
-      const bool v1 = full || n0 + 2 * ip + 1 < ch.end;
-      vmask[ip] = (v0 ? 0x0000ffffu : 0u) | (v1 ? 0xffff0000u : 0u);
-    }
+  // Wave w takes the steps at t0 + 16 w of every 64-token tile.  Every step
+  // refills its rows and the loop body runs all kDepth steps, also past the
+  // chunk end (those rows read as zero and add nothing): with the same loads
+  // on every path the compiler waits for exactly the rows a step uses.
+  auto step = [&](Rows& rows, long t0) {
+    u32x4 kf[4], vf[4];
+    build_step(rows, table_rows(gp, L, G.H), rtab, L, G.eps, zacc, kf, vf, mfma_row);
+    gp.advance(adt, ady, adx, G.H, G.W);
+    issue(rows, k, v, beta, t0 + kDepth * kTile + wave * kStep, ch.end, G.heads, L);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 ku = {kp[c][0], kp[c][1], kp[c][2], kp[c][3]};
-      const u32x4 vu = {sel_channel(r.v[0], r.v[1], c) & vmask[0], sel_channel(r.v[2], r.v[3], c) & vmask[1],
-                        sel_channel(r.v[4], r.v[5], c) & vmask[2], sel_channel(r.v[6], r.v[7], c) & vmask[3]};
-      *reinterpret_cast<u32x4*>(dst + c * kFragBytes + lane * 16) = ku;
-      *reinterpret_cast<u32x4*>(dst + (4 + c) * kFragBytes + lane * 16) = vu;
+      pk[c] = kf[c];
+      pv[c] = vf[c];
     }
   };
 
-  if constexpr (LDSR) lds_barrier();   // RoPE rows staged
-  Rows rows;
-  if (ch.begin < ch.end) issue(rows, ch.begin + wave * kStep);
-  for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
-    unsigned char* tile = smem;
-    if (t0 != ch.begin) lds_barrier();   // every wave is done with the previous tile's fragments
-    const long base = t0 + wave * kStep;
-    if (base < ch.end) {
-      const Rows cur = rows;
-      if (t0 + kTile < ch.end) issue(rows, base + kTile);   // prefetch this wave's next step
-      prepare(cur, base, tile + wave * kStepBytes);
-    } else {
-      if (t0 + kTile < ch.end) issue(rows, base + kTile);
-      // a step wholly past the chunk contributes nothing
+  Rows rr[kDepth];
 #pragma unroll
-      for (int f = 0; f < 8; ++f)
-        *reinterpret_cast<u32x4*>(tile + wave * kStepBytes + f * kFragBytes + lane * 16) = (u32x4){0u, 0u, 0u, 0u};
-    }
-    lds_barrier();
+  for (int d = 0; d < kDepth; ++d) issue(rr[d], k, v, beta, ch.begin + d * kTile + wave * kStep, ch.end, G.heads, L);
+  for (long t0 = ch.begin; t0 < ch.end; t0 += kDepth * kTile) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned char* st = tile + j * kStepBytes;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + (4 + wave) * kFragBytes + lane * 16));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(st + c * kFragBytes + lane * 16));
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
-      }
-    }
+    for (int d = 0; d < kDepth; ++d) step(rr[d], t0 + d * kTile);
   }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) mfma_row(a);   // the last step's MFMAs
 
-  // key sums: lanes m and m + 32 hold the same channels; then across waves
-  float* zred = reinterpret_cast<float*>(smem);   // [4 waves][128]
-  lds_barrier();
-#pragma unroll
-  for (int c = 0; c < 4; ++c) zacc[c] += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) * 4, __float_as_int(zacc[c])));
-  if (h == 0) *reinterpret_cast<f32x4*>(zred + wave * 128 + 4 * m) = (f32x4){zacc[0], zacc[1], zacc[2], zacc[3]};
-  lds_barrier();
+  // Sum the 4 waves' states in two rounds of two v-side slots: every wave
+  // stores its half as [a'][r][lane][c] (the 4 k-side slots of one output row
+  // next to each other), then every thread adds the 4 copies in wave order
+  // (the same result on every run) and writes rows of the partial.
   float* dst = partial + ((size_t)ch.head * G.nseg * G.cps1 + ch.index) * (size_t)(D * D + D);
-  if (wave == 0 && lane < 32) {
-    f32x4 zz = *reinterpret_cast<const f32x4*>(zred + 4 * m);
+  write_key_sum(zacc, zred, dst, L, wave);   // its barrier also retires the table
 #pragma unroll
-    for (int wv = 1; wv < 4; ++wv) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(zred + wv * 128 + 4 * m);
-      zz.x += o.x; zz.y += o.y; zz.z += o.z; zz.w += o.w;
+  for (int R = 0; R < 2; ++R) {
+    if (R == 1) lds_barrier();   // round 0 read out
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<f32x4*>(smem + wave * kHalfBytes + ((a2 * 16 + r) * 64 + L.lane) * 16) =
+            (f32x4){acc[2 * R + a2][0][r], acc[2 * R + a2][1][r], acc[2 * R + a2][2][r], acc[2 * R + a2][3][r]};
+    lds_barrier();
+    // S[4 mr + a][4 n + c] with mr = 8(r/4) + 4h + r%4, n = lane % 32
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = (int)threadIdx.x + j * kThreads;   // (a' * 16 + r) * 64 + lane
+      const int ln = e & 63, r = (e >> 6) & 15, a = 2 * R + (e >> 10);
+      const int mr = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
+      f32x4 sum = *reinterpret_cast<const f32x4*>(smem + e * 16);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(smem + w * kHalfBytes + e * 16);
+        sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
+      }
+      *reinterpret_cast<f32x4*>(dst + (4 * mr + a) * D + 4 * (ln & 31)) = sum;
     }
-    *reinterpret_cast<f32x4*>(dst + D * D + 4 * m) = zz;
-  }
-  // S[4 mr + wave][4 n + c] with mr = 8(r/4) + 4h + r%4, n = lane % 32
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int mr = 8 * (r >> 2) + 4 * h + (r & 3);
-    *reinterpret_cast<f32x4*>(dst + (4 * mr + wave) * D + 4 * m) = (f32x4){acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
   }
 }
 
@@ -442,15 +589,9 @@ hipError_t launch_state_partial(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   const int blocks = G.heads * G.nseg * G.cps1;
   if constexpr (D == 128 && Elem<E>::is_bf16) {
-    if (G.pass1_reg) {
-      if (G.rope_lds1)
-        hipLaunchKernelGGL((state_partial_frag_kernel<true>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.beta, (const float2*)a.rope,
-                           a.partial, G);
-      else
-        hipLaunchKernelGGL((state_partial_frag_kernel<false>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.beta, (const float2*)a.rope,
-                           a.partial, G);
+    if (G.pass1_reg) {   // the planner sets it only with the RoPE rows in LDS
+      hipLaunchKernelGGL(state_partial_acc_kernel, dim3(blocks), dim3(kThreads), 0, a.stream, (const bf16_t*)a.k,
+                         (const bf16_t*)a.v, (const bf16_t*)a.beta, (const float2*)a.rope, a.partial, G);
       return hipGetLastError();
     }
   }

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL */
-  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, eps not finite/positive, size overflow */
+  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, eps not finite or below FLT_MIN, size overflow */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
   GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
@@ -72,7 +72,8 @@ typedef enum {
  *   rms_w      : [d] float32, output RMSNorm weight          (read)
  *   out        : [N, heads, d] in `dtype`                    (written; must not alias an input)
  *   T, H, W    : latent grid (frames, rows, columns), each >= 0; N = 0 is a no-op
- *   heads      : >= 1;  d : 32, 64 or 128;  eps : finite, > 0
+ *   heads      : >= 1;  d : 32, 64 or 128;  eps : finite, >= FLT_MIN (a normal float, so
+ *                rsqrt(mean(x^2) + eps) stays finite for an all-zero row)
  * When N == 0 the tensor pointers may be NULL.
  * Returns GLA_OK or a negative gla_status.
  */

@@ -6,6 +6,12 @@ import numpy as np
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}   # max|err| <= TOL * max|ref|
 
+# Key-sum state z.  For bf16 inputs the HIP path multiplies each token's phi(k)
+# by its RMS factor rounded to bf16 (relative error <= 2^-9); every term of z
+# is non-negative, so each channel's sum keeps that relative bound.  fp32
+# accumulation over the sequence adds far less.
+Z_TOL = {"f32": 1e-5, "bf16": 2.5e-3}
+
 
 def torch_mod():
     import torch

@@ -75,7 +75,7 @@ def test_shape_errors(lib):
     assert fwd(lib, T=-1) == E_SHAPE
     assert fwd(lib, W=-3) == E_SHAPE
     assert fwd(lib, heads=0) == E_SHAPE
-    for eps in (0.0, -1e-6, math.nan, math.inf):
+    for eps in (0.0, -1e-6, math.nan, math.inf, 1e-40):   # 1e-40 is subnormal
         assert fwd(lib, eps=eps) == E_SHAPE
     assert fwd(lib, T=2000, H=2000, W=2000) == E_SHAPE       # N >= 2^31
     assert fwd(lib, T=1000, H=1000, W=1000, heads=64, d=128) == E_SHAPE  # N*heads*d >= 2^40
