@@ -62,15 +62,19 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Buffer resources based at this chunk's first row and head, so offsets
-  // stay small whatever the tensor size; rows past the sequence read as zero.
+  // Every tile's loads and stores go through buffer resources based at the
+  // tile's first row and this head and ending at the chunk's last row: rows
+  // past it read as zero and stores to them are dropped, so no path needs a
+  // mask and every path issues the same memory operations (the compiler's
+  // waits then cover exactly the rows in use).
   const uint32_t ROW = (uint32_t)G.heads * D * sizeof(E);
-  const size_t base_off = (size_t)ch.begin * ROW + (size_t)ch.head * D * sizeof(E);
-  const uint64_t rest = (uint64_t)(G.N - ch.begin) * ROW - (uint64_t)ch.head * D * sizeof(E);
-  const uint32_t nrec = rest > 0xffffffffull ? 0xffffffffu : (uint32_t)rest;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const char*>(q) + base_off, nrec);
-  const __amdgpu_buffer_rsrc_t grs = make_rsrc(reinterpret_cast<const char*>(g) + base_off, nrec);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(reinterpret_cast<const char*>(out) + base_off, nrec);
+  const uint32_t head_off = (uint32_t)ch.head * D * sizeof(E);
+  auto tile_rsrc = [&](const void* p, long t0) {
+    const long left = ch.end - t0;
+    const uint32_t rows = left <= 0 ? 0u : (left >= kT ? (uint32_t)kT : (uint32_t)left);
+    const uint32_t bytes = rows == 0 ? 0u : rows * ROW - head_off;   // the last row ends at this head's D channels
+    return make_rsrc(reinterpret_cast<const char*>(p) + (size_t)t0 * ROW + head_off, bytes);
+  };
   uint32_t voff[C::TPT];
 #pragma unroll
   for (int i = 0; i < C::TPT; ++i) voff[i] = (uint32_t)(tg * C::TPT + i) * ROW + 8u * cg * sizeof(E);
@@ -112,21 +116,18 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   // Two tiles of q/g rows in flight: buffers A and B alternate.
   Raw qa[C::TPT], ga[C::TPT], qb[C::TPT], gb[C::TPT];
   auto issue = [&](Raw (&qr)[C::TPT], Raw (&gr)[C::TPT], long t0) {
-    const uint32_t soff = (uint32_t)(t0 - ch.begin) * ROW;
+    const __amdgpu_buffer_rsrc_t qrs = tile_rsrc(q, t0), grs = tile_rsrc(g, t0);
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
-      qr[i] = BR::load(qrs, voff[i], soff);
-      gr[i] = BR::load(grs, voff[i], soff);
+      qr[i] = BR::load(qrs, voff[i], 0);
+      gr[i] = BR::load(grs, voff[i], 0);
     }
   };
-  if (ch.begin < ch.end) issue(qa, ga, ch.begin);
-  if (ch.begin + kT < ch.end) issue(qb, gb, ch.begin + kT);
+  issue(qa, ga, ch.begin);
+  issue(qb, gb, ch.begin + kT);
   if constexpr (LDSR) lds_barrier();
 
   auto tile = [&](Raw (&qr)[C::TPT], Raw (&gr)[C::TPT], long t0) {
-    const uint32_t soff = (uint32_t)(t0 - ch.begin) * ROW;
-    const uint32_t soff_next = (uint32_t)(t0 + 2 * kT - ch.begin) * ROW;
-    const bool refill = t0 + 2 * kT < ch.end;   // uniform
     // RoPE entries of this tile's tokens
     typename R::CS cs[C::TPT];
     GridPos pp = pos;
@@ -181,9 +182,10 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       }
     }
     // q rows consumed: refill with the rows two tiles ahead
-    if (refill) {
+    {
+      const __amdgpu_buffer_rsrc_t qrs = tile_rsrc(q, t0 + 2 * kT);
 #pragma unroll
-      for (int i = 0; i < C::TPT; ++i) qr[i] = BR::load(qrs, voff[i], soff_next);
+      for (int i = 0; i < C::TPT; ++i) qr[i] = BR::load(qrs, voff[i], 0);
     }
     // rq tile complete; every wave has also finished reading the previous
     // tile's nums, so they may be overwritten below
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
     // nums complete; every wave has also finished reading rq
     lds_barrier();
 
-    const bool full = t0 + kT <= ch.end;   // uniform
+    const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
       const float* src = nums + (tg * C::TPT + i) * C::NUM_PITCH + 8 * cg;
@@ -230,18 +232,21 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
-      if (full || t0 + tg * C::TPT + i < ch.end) BR::store(ors, voff[i], soff, Elem<E>::pack(y));
+      BR::store(ors, voff[i], 0, Elem<E>::pack(y));   // rows past the chunk are dropped
     }
     // g rows consumed: refill with the rows two tiles ahead
-    if (refill) {
+    {
+      const __amdgpu_buffer_rsrc_t grs = tile_rsrc(g, t0 + 2 * kT);
 #pragma unroll
-      for (int i = 0; i < C::TPT; ++i) gr[i] = BR::load(grs, voff[i], soff_next);
+      for (int i = 0; i < C::TPT; ++i) gr[i] = BR::load(grs, voff[i], 0);
     }
   };
 
+  // Both tiles of the body run also past the chunk end (their rows read as
+  // zero and their stores are dropped).
   for (long t0 = ch.begin; t0 < ch.end; t0 += 2 * kT) {
     tile(qa, ga, t0);
-    if (t0 + kT < ch.end) tile(qb, gb, t0 + kT);
+    tile(qb, gb, t0 + kT);
   }
 }
 
