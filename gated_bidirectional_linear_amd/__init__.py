@@ -121,19 +121,21 @@ def forward(q, k, v, beta, g, rms_w, grid, eps: float = 1e-6, out=None, stream=N
 
 
 def block_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, block_frames: int,
-                         eps: float = 1e-6, out=None, stream=None):
+                         eps: float = 1e-6, out=None, stream=None, t_offset: int = 0):
     """Block-causal operator.  ``state_S`` [heads, d, d] and ``state_z`` [heads, d]
     (float32) are read as the carried state and overwritten in place with the
-    state after the last block.  Returns ``out``."""
+    state after the last block.  ``t_offset`` is the absolute frame of the
+    call's first frame (a multiple of ``block_frames``) when a long video is
+    streamed through successive calls.  Returns ``out``."""
     torch = _torch()
     T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
     _check("state_S", state_S, (heads, d, d), torch.float32, q.device)
     _check("state_z", state_z, (heads, d), torch.float32, q.device)
-    st = load().gla_block_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
-                                         heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
-                                         _ptr(state_S), _ptr(state_z), int(block_frames), code)
+    st = load().gla_block_causal_forward_at(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
+                                            heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
+                                            _ptr(state_S), _ptr(state_z), int(block_frames), int(t_offset), code)
     if st != 0:
-        raise GlaError(st, "gla_block_causal_forward")
+        raise GlaError(st, "gla_block_causal_forward_at")
     return out
 
 

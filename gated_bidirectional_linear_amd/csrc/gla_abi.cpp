@@ -190,14 +190,15 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
 
 int run(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w, int T,
         int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S, float* z,
-        int block_frames) {
+        int block_frames, int t_offset) {
   const bool causal = S != nullptr || z != nullptr || block_frames > 0;
   const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z, block_frames);
   if (st != GLA_OK) return st;
   const long long N = (long long)T * H * W;
   if (N == 0) return GLA_OK;
 
-  const Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0, dtype == GLA_DTYPE_BF16);
+  Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0, dtype == GLA_DTYPE_BF16);
+  G.t_offset = t_offset;
   const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
@@ -248,25 +249,36 @@ extern "C" {
 
 int gla_forward(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
                 int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype) {
-  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr, nullptr, 0);
+  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr, nullptr, 0, 0);
+}
+
+int gla_block_causal_forward_at(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                                const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                                void* stream, float* state_S, float* state_z, int block_frames, int t_offset,
+                                int dtype) {
+  const bool frames_ok = block_frames >= 1 && t_offset >= 0 && t_offset % block_frames == 0 &&
+                         (long long)t_offset + T <= INT32_MAX;
+  if (!frames_ok) {
+    // validate the rest first so dtype/d errors keep their precedence
+    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
+    return st != GLA_OK ? st : GLA_ERR_SHAPE;
+  }
+  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S, state_z, block_frames,
+             t_offset);
 }
 
 int gla_block_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
                              const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
                              void* stream, float* state_S, float* state_z, int block_frames, int dtype) {
-  if (block_frames < 1) {
-    // validate the rest first so dtype/d errors keep their precedence
-    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
-    return st != GLA_OK ? st : GLA_ERR_SHAPE;
-  }
-  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S, state_z, block_frames);
+  return gla_block_causal_forward_at(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, state_S, state_z,
+                                     block_frames, 0, dtype);
 }
 
 const char* gla_status_string(int status) {
   switch (status) {
     case GLA_OK: return "ok";
     case GLA_ERR_NULL: return "a required pointer is NULL";
-    case GLA_ERR_SHAPE: return "invalid shape, block size, eps or size overflow";
+    case GLA_ERR_SHAPE: return "invalid shape, block size, frame offset, eps or size overflow";
     case GLA_ERR_DTYPE: return "unknown dtype";
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case GLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
@@ -277,7 +289,7 @@ const char* gla_status_string(int status) {
   }
 }
 
-int gla_version(void) { return (1 << 16) | 0; }
+int gla_version(void) { return (1 << 16) | 1; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

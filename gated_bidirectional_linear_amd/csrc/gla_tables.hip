@@ -8,7 +8,9 @@ namespace gla {
 // 1. RoPE tables
 // ===========================================================================
 template <int D>
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W) {
+// Frame t of the call sits at absolute frame t_offset + t (streaming across
+// calls); rows and columns always start at 0.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W, int t_offset) {
   using R = Rope<D>;
   const long total = (long)T * R::PT + (long)H * R::PY + (long)W * R::PX;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -16,7 +18,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
   long pos, i;
   int da;
   if (idx < (long)T * R::PT) {
-    pos = idx / R::PT; i = idx % R::PT; da = D / 4;
+    pos = idx / R::PT + t_offset; i = idx % R::PT; da = D / 4;
   } else if (idx < (long)T * R::PT + (long)H * R::PY) {
     const long r = idx - (long)T * R::PT;
     pos = r / R::PY; i = r % R::PY; da = 3 * D / 8;
@@ -66,7 +68,7 @@ hipError_t launch_rope_table(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   const long total = (long)G.T * (D / 8) + (long)G.H * (3 * D / 16) + (long)G.W * (3 * D / 16);
   const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL((rope_table_kernel<D>), dim3(blocks), dim3(256), 0, a.stream, a.rope, G.T, G.H, G.W);
+  hipLaunchKernelGGL((rope_table_kernel<D>), dim3(blocks), dim3(256), 0, a.stream, a.rope, G.T, G.H, G.W, G.t_offset);
   return hipGetLastError();
 }
 

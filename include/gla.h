@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL */
-  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, eps not finite or below FLT_MIN, size overflow */
+  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, bad t_offset, eps not finite or below FLT_MIN, size overflow */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
   GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
@@ -99,6 +99,28 @@ int gla_block_causal_forward(const void* q, const void* k, const void* v, const 
                              const void* g, const float* rms_w, int T, int H, int W, int heads,
                              int d, float eps, void* out, void* stream, float* state_S,
                              float* state_z, int block_frames, int dtype);
+
+/*
+ * The block-causal operator for one piece of a longer video streamed through
+ * successive calls: the carried state is the constant-memory cache that lets
+ * generation go on block after block up to minute-long videos (SANA-Video
+ * notes, overview and key design 2).
+ *
+ * Same arguments as gla_block_causal_forward, plus
+ *   t_offset : absolute latent frame of this call's frame 0, >= 0 and a
+ *              multiple of block_frames (a block cannot straddle two calls,
+ *              since its tokens also read the block's later tokens);
+ *              t_offset + T <= INT32_MAX.
+ * The RoPE position of frame t is t_offset + t; rows and columns start at 0.
+ * Calling with frames [0, T1) and then, on the returned state, with frames
+ * [T1, T) and t_offset = T1 (T1 a multiple of block_frames) gives the output
+ * and state of one call over [0, T).  gla_block_causal_forward is this call
+ * with t_offset = 0.  A bad t_offset returns GLA_ERR_SHAPE.
+ */
+int gla_block_causal_forward_at(const void* q, const void* k, const void* v, const void* beta,
+                                const void* g, const float* rms_w, int T, int H, int W, int heads,
+                                int d, float eps, void* out, void* stream, float* state_S,
+                                float* state_z, int block_frames, int t_offset, int dtype);
 
 /* Static text for a gla_status value (never NULL). */
 const char* gla_status_string(int status);

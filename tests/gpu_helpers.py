@@ -62,7 +62,7 @@ def run_forward(dev: dict, grid, eps):
     return out
 
 
-def run_block_causal(dev: dict, grid, eps, block_frames, S0=None, z0=None):
+def run_block_causal(dev: dict, grid, eps, block_frames, S0=None, z0=None, t_offset=0):
     import gated_bidirectional_linear_amd as gla
     torch = torch_mod()
     N, heads, d = dev["q"].shape
@@ -72,6 +72,6 @@ def run_block_causal(dev: dict, grid, eps, block_frames, S0=None, z0=None):
         S.copy_(torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)))
         z.copy_(torch.from_numpy(np.ascontiguousarray(z0, dtype=np.float32)))
     out = gla.block_causal_forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], grid,
-                                   S, z, block_frames, eps=eps)
+                                   S, z, block_frames, eps=eps, t_offset=t_offset)
     torch.cuda.synchronize()
     return out, S, z

@@ -39,6 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
+    assert lib.gla_version() & 0xFFFF >= 1          # 1.1: gla_block_causal_forward_at
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
@@ -61,6 +62,23 @@ def bc(lib, F=1, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
     p = list(P if ptrs is None else ptrs)
     return lib.gla_block_causal_forward(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None,
                                         p[7], p[8], F, dtype)
+
+
+def bc_at(lib, F=1, t_offset=0, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_block_causal_forward_at(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None,
+                                           p[7], p[8], F, t_offset, dtype)
+
+
+def test_frame_offset_errors(lib):
+    assert bc_at(lib, F=2, t_offset=-2) == E_SHAPE
+    assert bc_at(lib, F=3, t_offset=4) == E_SHAPE              # not a whole number of blocks
+    assert bc_at(lib, F=1, t_offset=2**31 - 2, T=5) == E_SHAPE  # t_offset + T past INT32_MAX
+    assert bc_at(lib, F=0, t_offset=0) == E_SHAPE
+    assert bc_at(lib, F=2, t_offset=-2, dtype=7) == E_DTYPE    # dtype keeps its precedence
+    nulls = [None] * 10
+    assert bc_at(lib, F=3, t_offset=6, T=0, ptrs=nulls) == OK   # empty grid, valid offset
+    assert bc_at(lib, F=3, t_offset=6, ptrs=[None] + P[1:]) == E_NULL
 
 
 def test_dtype_and_head_dim_errors(lib):

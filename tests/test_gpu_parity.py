@@ -207,6 +207,59 @@ def test_block_causal_with_prior_state(dtype):
     assert rel_err(to_f64(z), rz) <= Z_TOL[dtype]
 
 
+def _frames(inp, t0, t1, hw):
+    part = {k: (v[t0 * hw: t1 * hw] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+    part["grid"] = (t1 - t0,) + tuple(inp["grid"][1:])
+    return part
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_streaming_chained_calls_equal_one_call(dtype):
+    """A video streamed through three calls with frame offsets gives the output
+    and final state of one call (and of the oracle)."""
+    T, H, W, heads, d, F = 9, 6, 7, 2, 128, 3
+    hw = H * W
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=21)
+    one, S1, z1 = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F)
+    S, z = None, None
+    outs = []
+    for t0, t1 in ((0, 3), (3, 6), (6, 9)):
+        part = _frames(inp, t0, t1, hw)
+        o, S_t, z_t = run_block_causal(to_device(part), part["grid"], part["eps"], F, S, z, t_offset=t0)
+        outs.append(to_f64(o))
+        S, z = S_t.cpu().numpy(), z_t.cpu().numpy()
+    chained = np.concatenate(outs)
+    ro, rS, rz = _oracle_bc(inp, F)
+    err = rel_err(chained, ro)
+    _report(f"streamed 3 calls {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+    # the same kernels on the same values: one call and the chain agree closely
+    assert rel_err(chained, to_f64(one)) <= (1e-6 if dtype == "f32" else 1e-2)
+    assert rel_err(S.astype(np.float64), to_f64(S1)) <= 1e-5
+    assert rel_err(z.astype(np.float64), to_f64(z1)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_streaming_large_frame_offset(dtype):
+    """Frames far into a video: RoPE positions t_offset + t against the oracle
+    with the same position offset, from a carried oracle state."""
+    T, H, W, heads, F, t_off = 4, 5, 6, 2, 2, 1000
+    d = 64 if dtype == "f32" else 128   # the bf16 case runs the register-accumulating pass 1
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=22)
+    S0, z0 = make_state(heads, d, seed=3)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F, S0, z0, t_offset=t_off)
+    ro, rS, rz = _oracle_bc(inp, F, S0=S0, z0=z0, pos_offset=(t_off, 0, 0))
+    err = rel_err(to_f64(out), ro)
+    _report(f"frame offset {t_off} {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+    assert rel_err(to_f64(S), rS) <= (1e-5 if dtype == "f32" else 1e-2)
+    assert rel_err(to_f64(z), rz) <= Z_TOL[dtype]
+    # the offset matters: without it the oracle's output moves by far more
+    # than the kernel's error (so this test would catch an ignored offset)
+    plain = _oracle_bc(inp, F, S0=S0, z0=z0)[0]
+    assert rel_err(plain, ro) > max(10 * err, TOL[dtype])
+
+
 def test_block_causal_final_state_equals_bidirectional_state():
     inp = make_inputs(6, 5, 7, 2, 128, "f32", seed=15)
     _, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], 2)
