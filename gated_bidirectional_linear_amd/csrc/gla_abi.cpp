@@ -25,6 +25,8 @@ constexpr int kDefaultTargetWg1 = 512;
 // one workgroup per CU.
 constexpr int kDefaultTargetWgAcc1 = 256;
 constexpr int kDefaultTargetWg2 = 2048;
+// The paired-head output kernel (bf16, d = 128) runs two workgroups per CU.
+constexpr int kDefaultTargetWgPair2 = 1024;
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -68,7 +70,11 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
   G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
 
-  const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", kDefaultTargetWg2), per_seg_heads);
+  // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128
+  G.pass2_pair = (bf16 && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
+  const int per_seg_units2 = G.pass2_pair ? per_seg_heads / 2 : per_seg_heads;
+  const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", G.pass2_pair ? kDefaultTargetWgPair2 : kDefaultTargetWg2),
+                             per_seg_units2);
   int cps2 = want2 < 1 ? 1 : want2;
   if (cps2 > tiles_per_seg) cps2 = tiles_per_seg;
   while (!rope_fits((long)ceil_div(tiles_per_seg, cps2) * kTile) && cps2 < tiles_per_seg) ++cps2;
@@ -76,8 +82,9 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
-  // the register-accumulating kernel reads its RoPE rows from LDS only
+  // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
   if (!G.rope_lds1) G.pass1_reg = 0;
+  if (!G.rope_lds2) G.pass2_pair = 0;
   return G;
 }
 

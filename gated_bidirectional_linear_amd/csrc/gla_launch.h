@@ -45,6 +45,7 @@ struct Geometry {
   int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
   int rope_lds2;  // same for pass 2
   int pass1_reg;  // pass 1 uses the register-accumulating kernel (bf16, d = 128, RoPE rows in LDS)
+  int pass2_pair; // pass 2 takes heads in pairs (bf16, d = 128, even heads, RoPE rows in LDS)
   int t_offset;   // absolute frame of the call's frame 0 (RoPE positions only)
   float eps;
 };

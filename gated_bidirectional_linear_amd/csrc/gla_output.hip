@@ -250,9 +250,238 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   }
 }
 
+// ===========================================================================
+// Fused output for bf16, d = 128, heads taken in pairs: two workgroups per CU.
+//
+// HBM serves this op's mix of short reads and writes better when a
+// workgroup's rows are wider: with two heads per workgroup every token row
+// segment read or written is 512 contiguous bytes instead of 256 (a copy of
+// the same shape measured ~640 against ~750 us at 720p/60s).  256 threads:
+// lane group cg = tid % 32 holds 8 channels (head cg / 16, channels
+// 8 (cg % 16)..+7) of token tg = tid / 32 + 8 i (i = 0..3) of each 32-token
+// tile; rows are fetched two tiles ahead through buffer resources that end
+// at the chunk (rows past it read as zero, stores to them are dropped).  Two
+// workgroups share a CU, so one's MFMAs overlap the other's vector work.  Wave
+// w multiplies head w / 2's rotated queries by two 32-row tiles of its state
+// (16 A-fragments in registers).  The per-token math is the same as in
+// output_kernel.
+// ===========================================================================
+namespace pair2 {
+constexpr int D = 128;
+constexpr int HP = 2;                 // heads per workgroup
+constexpr int TILE = 32;              // tokens per tile
+constexpr int TPI = kThreads / (HP * D / 8);   // tokens per load instruction (8)
+constexpr int TPT = TILE / TPI;       // tokens per thread per tile (4)
+constexpr int DEPTH = 2;              // tiles of rows in flight
+constexpr int RQ_PITCH = D + 8;       // bf16 elements per (token, head) row
+constexpr int NUM_PITCH = D + 4;      // floats per (token, head) row
+constexpr int RQ_BYTES = TILE * HP * RQ_PITCH * 2;
+constexpr int NUM_BYTES = TILE * HP * NUM_PITCH * 4;
+constexpr int KSTEPS = D / 16;
+}  // namespace pair2
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void output_pair_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ g, const float* __restrict__ states,
+    const float* __restrict__ rms_w, const float2* __restrict__ rope, bf16_t* __restrict__ out, Geometry G) {
+  using namespace pair2;
+  using R = Rope<D>;
+  using M = Mfma<bf16_t>;
+  constexpr int SZ = D * D + D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RQ_BYTES + NUM_BYTES + kRopeLdsEntries * 8];
+  bf16_t* rqs = reinterpret_cast<bf16_t*>(smem);                 // [TILE][HP][RQ_PITCH]
+  float* nums = reinterpret_cast<float*>(smem + RQ_BYTES);       // [TILE][HP][NUM_PITCH]
+
+  // chunk-major over head pairs: consecutive ids take the same token range
+  const int npairs = G.heads / HP;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int ci = lin / npairs;
+  const int pair = lin - ci * npairs;
+  const int seg = ci / G.cps2;
+  const long s0 = (long)seg * G.seg_len;
+  const long s1 = min(s0 + (long)G.seg_len, (long)G.N);
+  const long cbeg = min(s0 + (long)(ci - seg * G.cps2) * G.chunk2, s1);
+  const long cend = min(cbeg + (long)G.chunk2, s1);
+  const int h0 = HP * pair;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int cg = tid & 31;              // lane group within a token's 512 bytes
+  const int hl = cg >> 4;               // head of the pair
+  const int c16 = cg & 15;              // channels 8 c16 .. 8 c16 + 7
+  const int tg = tid >> 5;              // token within an instruction
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const uint32_t ROW = (uint32_t)G.heads * D * 2;
+  const uint32_t pair_off = (uint32_t)h0 * D * 2;
+  auto tile_rsrc = [&](const void* p, long t0) {
+    const long left = cend - t0;
+    const uint32_t rows = left <= 0 ? 0u : (left >= TILE ? (uint32_t)TILE : (uint32_t)left);
+    const uint32_t bytes = rows == 0 ? 0u : rows * ROW - pair_off;   // the last row ends at this pair's channels
+    return make_rsrc(reinterpret_cast<const char*>(p) + (size_t)t0 * ROW + pair_off, bytes);
+  };
+  uint32_t voff[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + tg) * ROW + (uint32_t)hl * D * 2 + 16u * c16;
+
+  // this wave's head and its two 32-row tiles of S as A-fragments
+  const int hw = wave >> 1;
+  const float* Sw = states + ((size_t)seg * G.heads + h0 + hw) * SZ;
+  typename M::frag sfrag[2][KSTEPS];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const float* srow = Sw + (size_t)(32 * (2 * (wave & 1) + v) + l32) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(srow + 16 * ks + 8 * hi);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(srow + 16 * ks + 8 * hi + 4);
+      const float tmp[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      sfrag[v][ks] = M::from_f32(tmp);
+    }
+  }
+  const float* zrow = states + ((size_t)seg * G.heads + h0 + hl) * SZ + D * D;
+  float zc[8], wc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    zc[c] = zrow[8 * c16 + c];
+    wc[c] = rms_w[8 * c16 + c];
+  }
+
+  const typename R::View rv = rope_view<D, true>(reinterpret_cast<float2*>(smem + RQ_BYTES + NUM_BYTES), rope, G,
+                                                 cbeg, cend);
+  const int t_last = cbeg < cend ? (int)((cend - 1) / (G.H * G.W)) : 0;
+  const int p0 = 4 * c16;   // this thread's 4 pairs share one axis
+  const int axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
+  const int rbase = axis == 0 ? p0 - rv.t_lo * R::PT
+                  : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
+  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+  // grid position of token tg of the current tile; tokens of a thread are TPI apart
+  const int HW = G.H * G.W;
+  GridPos pos;
+  pos.set((int)(cbeg + tg), G.H, G.W);
+  const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
+  const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
+
+  u32x4 qr[DEPTH][TPT], gr[DEPTH][TPT];
+  auto issue_q = [&](u32x4 (&r)[TPT], long t0) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+  };
+  auto issue_g = [&](u32x4 (&r)[TPT], long t0) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    issue_q(qr[d], cbeg + d * TILE);
+    issue_g(gr[d], cbeg + d * TILE);
+  }
+  lds_barrier();   // RoPE rows staged
+
+  // One tile.  Every path issues the same memory operations (rows past the
+  // chunk read as zero, their stores are dropped), so the compiler's waits
+  // cover exactly the rows in use.
+  auto tile = [&](u32x4 (&qt)[TPT], u32x4 (&gt)[TPT], long t0) {
+    float rden[TPT];
+    GridPos pp = pos;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tc = pp.t < t_last ? pp.t : t_last;
+      const int ps = axis == 0 ? tc : (axis == 1 ? pp.y : pp.x);
+      const f32x4* e = reinterpret_cast<const f32x4*>(rv.tab + rbase + ps * rstride);
+      const f32x4 ca = e[0], cb = e[1];
+      typename R::CS cs;
+      cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
+      cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
+      pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
+
+      const u32x4 u = qt[i];
+      float ss = dot2sq(u.x, 0.f);
+      ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
+      const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
+      float ph[8];
+      Elem<bf16_t>::unpack(rl, ph);
+      float dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
+      ss = group_sum<16>(ss);
+      dp = group_sum<16>(dp);
+      const float ms = ss * (1.0f / D) + G.eps;
+      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
+      rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * r);
+      R::apply(ph, cs);
+      *reinterpret_cast<u32x4*>(rqs + ((i * TPI + tg) * HP + hl) * RQ_PITCH + 8 * c16) = Elem<bf16_t>::pack(ph);
+    }
+    pos.advance(t_dt, t_dy, t_dx, G.H, G.W);
+    issue_q(qt, t0 + DEPTH * TILE);   // q rows consumed: refill DEPTH tiles ahead
+    // rq tile complete; every wave has also finished reading the previous
+    // tile's nums, so they may be overwritten below
+    lds_barrier();
+
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const typename M::frag b = M::lds_frag(rqs + (l32 * HP + hw) * RQ_PITCH + ks * 16 + 8 * hi);
+        acc = M::mma(sfrag[v][ks], b, acc);
+      }
+      // C[m = v channel 8(r/4) + 4 hi + r%4 of the tile][n = token l32]
+      float* row = nums + (l32 * HP + hw) * NUM_PITCH + 32 * (2 * (wave & 1) + v) + 4 * hi;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<f32x4*>(row + 8 * rb) = (f32x4){acc[4 * rb], acc[4 * rb + 1], acc[4 * rb + 2], acc[4 * rb + 3]};
+    }
+    // nums complete; every wave has also finished reading rq
+    lds_barrier();
+
+    const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const float* src = nums + ((i * TPI + tg) * HP + hl) * NUM_PITCH + 8 * c16;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      float gv[8];
+      Elem<bf16_t>::unpack(gt[i], gv);
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));   // sigmoid(g) * num
+        ss += y[c] * y[c];
+      }
+      ss = group_sum<16>(ss);
+      const float rd = rden[i];
+      const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
+      buf_store16(ors, voff[i], 0, Elem<bf16_t>::pack(y));   // rows past the chunk are dropped
+    }
+    issue_g(gt, t0 + DEPTH * TILE);   // g rows consumed: refill DEPTH tiles ahead
+  };
+
+  for (long t0 = cbeg; t0 < cend; t0 += DEPTH * TILE) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) tile(qr[d], gr[d], t0 + d * TILE);
+  }
+}
+
 template <int D, typename E>
 hipError_t launch_output(const LaunchArgs& a) {
   const Geometry& G = a.geo;
+  if constexpr (D == 128 && Elem<E>::is_bf16) {
+    if (G.pass2_pair) {   // the planner sets it only for an even head count with the RoPE rows in LDS
+      hipLaunchKernelGGL(output_pair_kernel, dim3((G.heads / 2) * G.nseg * G.cps2), dim3(kThreads), 0, a.stream,
+                         (const bf16_t*)a.q, (const bf16_t*)a.g, (const float*)a.states, a.rms_w,
+                         (const float2*)a.rope, (bf16_t*)a.out, G);
+      return hipGetLastError();
+    }
+  }
   const int blocks = G.heads * G.nseg * G.cps2;
   if (G.rope_lds2)
     hipLaunchKernelGGL((output_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.q,

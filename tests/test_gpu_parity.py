@@ -315,11 +315,25 @@ def test_chunking_variants(monkeypatch, wg1, wg2):
 @pytest.mark.parametrize("shape", [(5, 9, 13, 3, 128), (3, 22, 40, 2, 128), (1, 1, 1, 2, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_generic_pass1_kernel_bf16(monkeypatch, shape):
-    """The LDS-staged pass-1 kernel on bf16 d=128 (the register-resident one is the default there)."""
+    """The LDS-staged pass-1 kernel on bf16 d=128 (the register-accumulating one is the default there)."""
     monkeypatch.setenv("GLA_PASS1_GENERIC", "1")
     T, H, W, heads, d = shape
     inp = make_inputs(T, H, W, heads, d, "bf16", seed=20)
     out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
     err = rel_err(out, _oracle(inp))
     _report(f"generic pass1 {shape}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(3, 22, 40, 2, 128), (4, 6, 7, 4, 128), (1, 1, 1, 2, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_one_head_output_kernel_bf16(monkeypatch, shape):
+    """The one-head-per-workgroup output kernel on bf16 d=128 with an even
+    head count (heads are taken in pairs by default there)."""
+    monkeypatch.setenv("GLA_PASS2_GENERIC", "1")
+    T, H, W, heads, d = shape
+    inp = make_inputs(T, H, W, heads, d, "bf16", seed=23)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"one-head output {shape}", err, TOL["bf16"])
     assert err <= TOL["bf16"]
