@@ -103,14 +103,15 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
     known_kib = calib_mib * 1024.0
     f_scale = known_kib / fetch[ck]
     w_scale = known_kib / write[ck]
-    for kernel in ("output_kernel", "state_partial"):
-        names = [k for k in fetch if kernel in k and k not in copy]
+    # every launch of a pass (whichever of its kernel variants ran) is summarised
+    # under the timing name of that pass
+    for prefix, short in (("gla::output", "output_kernel"), ("gla::state_partial", "state_partial_kernel")):
+        names = [k for k in fetch if k.startswith(prefix) and k not in copy]
         if not names:
             continue
         kn = names[0]
         fetched = fetch[kn] * f_scale * 1024
         written = write.get(kn, 0.0) * w_scale * 1024
-        short = "output_kernel" if kernel == "output_kernel" else "state_partial_kernel"
         path = os.path.join(ROOT, "profiles", f"{short}_{workload}_traffic.txt")
         with open(path, "w") as f:
             f.write(f"# HBM traffic of {short} on the {workload} workload, from rocprofv3 counters\n")
