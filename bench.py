@@ -43,7 +43,7 @@ def kernel_source_hash() -> str:
 
 def kernel_alg_bytes(w, kernel: str) -> int:
     """Algorithmic HBM bytes one launch of a kernel must move."""
-    s = 4 if w.dtype == "f32" else 2
+    s = w.elem_size
     big = w.N * w.heads * w.d * s
     if kernel == "output_kernel":        # read q, g; write out
         return 3 * big
@@ -164,7 +164,7 @@ def cpu_baseline(w, inp, heads_sample: int):
     except Exception:
         threads = 1
     heads = list(range(min(heads_sample, w.heads)))
-    sub = head_slice_f32(inp, heads) if w.dtype == "bf16" else {
+    sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
         **inp, **{n: inp[n][:, heads] for n in ("q", "k", "v", "g", "beta")}}
     t0 = time.perf_counter()
     orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"], sub["eps"])
@@ -186,6 +186,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="720p_60s")
+    ap.add_argument("--dtype", choices=("bf16", "fp8", "f32"), default=None,
+                    help="operator I/O dtype (default: the workload's own, bf16 for 720p_60s); "
+                         "fp8 = OCP FP8 E4M3 q, k, v, g, beta and out")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,6 +227,10 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     w = WORKLOADS[args.workload]
+    profiled = args.dtype is None or args.dtype == w.dtype   # profiles/ hold the default-dtype kernels
+    if args.dtype is not None:
+        import dataclasses
+        w = dataclasses.replace(w, dtype=args.dtype)
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: grid {w.T}x{w.H}x{w.W} N={w.N} heads={w.heads} d={w.d} {w.dtype}")
     t0 = time.time()
@@ -233,6 +240,8 @@ def main(argv=None):
     def upload(name):
         if w.dtype == "bf16":
             return torch.from_numpy(inp[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        if w.dtype == "fp8":
+            return torch.from_numpy(inp[name + "_bits"]).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(inp[name]).to(dev)
 
     # Working sets that would sit in the 256 MB Infinity Cache are rotated over
@@ -273,7 +282,7 @@ def main(argv=None):
     dom = max(("state_partial_kernel", "output_kernel"), key=lambda k: kt[k][0])
     dom_ms = kt[dom][0] / max(1, kt[dom][1])
     achieved = kernel_alg_bytes(w, dom) / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(dom, w.name)
+    traffic = read_traffic(dom, w.name) if profiled else None
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
 
@@ -303,7 +312,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": {"fp8": "fp8_e4m3"}.get(w.dtype, w.dtype),
         "data": "synthetic (seeded N(0,1) q,k,v,g; beta=sigmoid(N(0,1)); rms_w=1+0.1N(0,1))",
         "config": {
             "workload": w.name,

@@ -9,7 +9,7 @@ PyTorch provides device memory and streams.
     out = block_causal_forward(q, k, v, beta, g, rms_w, (T, H, W), state_S, state_z,
                                block_frames, eps=1e-6)
 
-q, k, v, g: [N, heads, d] (float32 or bfloat16, contiguous, on the GPU),
+q, k, v, g: [N, heads, d] (float32, bfloat16 or float8_e4m3fn, contiguous, on the GPU),
 beta: [N, heads] same dtype, rms_w: [d] float32, N = T*H*W, d in {32, 64, 128}.
 """
 from __future__ import annotations
@@ -31,10 +31,12 @@ __all__ = [
     "timing_read",
     "DTYPE_F32",
     "DTYPE_BF16",
+    "DTYPE_FP8_E4M3",
 ]
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_FP8_E4M3 = 2
 NUM_KERNELS = 4
 
 
@@ -63,7 +65,9 @@ def _dtype_code(t) -> int:
         return DTYPE_F32
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    if t.dtype == torch.float8_e4m3fn:
+        return DTYPE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float8_e4m3fn")
 
 
 def _check(name, t, shape, dtype, device):

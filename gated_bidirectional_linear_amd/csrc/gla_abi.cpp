@@ -37,7 +37,9 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames, bool bf16) {
+// narrow: the I/O dtype is bf16 or fp8, whose rows the fast d = 128 pass-1 kernel takes as bf16
+// words; bf16_io: the I/O dtype is bf16
+Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames, bool narrow, bool bf16_io) {
   Geometry G{};
   G.T = T; G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
   G.N = T * H * W;
@@ -57,7 +59,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
     return yx + frames * (d / 8) <= gla::kRopeLdsEntries;
   };
 
-  G.pass1_reg = (bf16 && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
+  G.pass1_reg = (narrow && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
   const int target1 = G.pass1_reg ? kDefaultTargetWgAcc1 : kDefaultTargetWg1;
   const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
@@ -70,8 +72,10 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
   G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
 
-  // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128
-  G.pass2_pair = (bf16 && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
+  // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128.  Its fp8
+  // instantiation spills registers at two workgroups per CU and measured slower than the
+  // one-head kernel, so fp8 keeps the one-head kernel.
+  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / 2 : per_seg_heads;
   const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", G.pass2_pair ? kDefaultTargetWgPair2 : kDefaultTargetWg2),
                              per_seg_units2);
@@ -163,7 +167,7 @@ Range range_of(const void* p, size_t bytes) {
 int validate(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
              int T, int H, int W, int heads, int d, float eps, const void* out, int dtype, bool causal,
              const float* S, const float* z, int block_frames) {
-  if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16) return GLA_ERR_DTYPE;
+  if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16 && dtype != GLA_DTYPE_FP8_E4M3) return GLA_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return GLA_ERR_UNSUPPORTED_D;
   if (T < 0 || H < 0 || W < 0 || heads < 1) return GLA_ERR_SHAPE;
   if (!(std::isfinite(eps) && eps >= FLT_MIN)) return GLA_ERR_SHAPE;
@@ -178,7 +182,7 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
     if (p == nullptr) return GLA_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return GLA_ERR_ALIGN;
-  const size_t es = dtype == GLA_DTYPE_BF16 ? 2 : 4;
+  const size_t es = dtype == GLA_DTYPE_BF16 ? 2 : (dtype == GLA_DTYPE_FP8_E4M3 ? 1 : 4);
   const size_t big = (size_t)N * heads * d * es;
   const Range rin[] = {range_of(q, big), range_of(k, big), range_of(v, big), range_of(g, big),
                        range_of(beta, (size_t)N * heads * es), range_of(rms_w, (size_t)d * 4)};
@@ -204,7 +208,8 @@ int run(const void* q, const void* k, const void* v, const void* beta, const voi
   const long long N = (long long)T * H * W;
   if (N == 0) return GLA_OK;
 
-  Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0, dtype == GLA_DTYPE_BF16);
+  Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0,
+                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16);
   G.t_offset = t_offset;
   const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
   const size_t sz = (size_t)d * d + d;
@@ -226,7 +231,7 @@ int run(const void* q, const void* k, const void* v, const void* beta, const voi
   a.rope = reinterpret_cast<float2*>(base);
   a.partial = reinterpret_cast<float*>(base + rope_bytes);
   a.states = reinterpret_cast<float*>(base + rope_bytes + part_bytes);
-  a.bf16 = dtype == GLA_DTYPE_BF16;
+  a.dtype = dtype;
   a.stream = hs;
   a.geo = G;
 
@@ -296,7 +301,7 @@ const char* gla_status_string(int status) {
   }
 }
 
-int gla_version(void) { return (1 << 16) | 1; }
+int gla_version(void) { return (1 << 16) | 2; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short bf16_t;  // bf16 storage
+typedef unsigned char fp8_t;    // OCP FP8 E4M3 (e4m3fn) storage
 
 constexpr int kTile = 64;       // tokens per staged tile
 constexpr int kThreads = 256;   // 4 waves of 64
@@ -37,6 +38,7 @@ template <typename E> struct Elem;
 
 template <> struct Elem<float> {
   static constexpr bool is_bf16 = false;
+  typedef float Lds;   // LDS staging / MFMA operand type
   struct Raw { f32x4 a, b; };  // 8 channels as loaded
   __device__ __forceinline__ static Raw load_raw(const float* p) {
     Raw r;
@@ -73,6 +75,7 @@ template <> struct Elem<float> {
 
 template <> struct Elem<bf16_t> {
   static constexpr bool is_bf16 = true;
+  typedef bf16_t Lds;
   typedef u32x4 Raw;  // 8 channels as loaded
   __device__ __forceinline__ static Raw load_raw(const bf16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -98,6 +101,46 @@ template <> struct Elem<bf16_t> {
   }
   __device__ __forceinline__ static void store_raw(bf16_t* p, const Raw& r) {
     __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+  }
+};
+
+// FP8 E4M3 (OCP e4m3fn: bias 7, no infinities, max 448).  gfx950's
+// v_cvt_pk_f32_fp8 / v_cvt_pk_fp8_f32 convert this format exactly and round
+// to nearest even (values at or past 480 become NaN; the operator's inputs and
+// outputs stay far below that).  Every e4m3 value is exact in bf16, so the
+// kernels stage fp8 operands as bf16 for the MFMA.
+template <> struct Elem<fp8_t> {
+  static constexpr bool is_bf16 = false;
+  typedef bf16_t Lds;
+  typedef u32x2 Raw;  // 8 channels as loaded
+  __device__ __forceinline__ static Raw load_raw(const fp8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  __device__ __forceinline__ static void unpack(const Raw& u, float (&x)[8]) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, true);
+    const f2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, true);
+    x[0] = a.x; x[1] = a.y; x[2] = b.x; x[3] = b.y; x[4] = c.x; x[5] = c.y; x[6] = d.x; x[7] = d.y;
+  }
+  __device__ __forceinline__ static void load8(const fp8_t* p, float (&x)[8]) { unpack(load_raw(p), x); }
+  __device__ __forceinline__ static Raw pack(const float (&x)[8]) {
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], w1, true);
+    return (u32x2){(uint32_t)w0, (uint32_t)w1};
+  }
+  __device__ __forceinline__ static void store8(fp8_t* p, const float (&x)[8]) {
+    __builtin_nontemporal_store(pack(x), reinterpret_cast<u32x2*>(p));
+  }
+  __device__ __forceinline__ static void store_raw(fp8_t* p, const Raw& r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+  }
+  __device__ __forceinline__ static float load1(const fp8_t* p) { return __builtin_amdgcn_cvt_f32_fp8((int)*p, 0); }
+  // bytes 2 SEL .. 2 SEL + 1 of w as a bf16 pair (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact)
+  template <bool SEL>
+  __device__ __forceinline__ static uint32_t bf16_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, SEL));
   }
 };
 
@@ -281,6 +324,15 @@ template <> struct BufRow<bf16_t> {
   }
   __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const Raw& v) {
     buf_store16(r, voff, soff, v);
+  }
+};
+template <> struct BufRow<fp8_t> {
+  typedef u32x2 Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const Raw& v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, 0);
   }
 };
 template <> struct BufRow<float> {

@@ -5,6 +5,7 @@
 namespace gla {
 
 typedef unsigned short bf16_t;
+typedef unsigned char fp8_t;
 
 template <int D> hipError_t launch_rope_table(const LaunchArgs& a);
 template <int D> hipError_t launch_state_reduce(const LaunchArgs& a);
@@ -33,13 +34,20 @@ static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
 }
 
 hipError_t launch_operator(const LaunchArgs& a, Timer& tm) {
-  if (a.bf16) {
+  // dtype codes of include/gla.h: 0 fp32, 1 bf16, 2 fp8 e4m3
+  if (a.dtype == 1) {
     switch (a.geo.d) {
       case 32: return launch_all<32, bf16_t>(a, tm);
       case 64: return launch_all<64, bf16_t>(a, tm);
       case 128: return launch_all<128, bf16_t>(a, tm);
     }
-  } else {
+  } else if (a.dtype == 2) {
+    switch (a.geo.d) {
+      case 32: return launch_all<32, fp8_t>(a, tm);
+      case 64: return launch_all<64, fp8_t>(a, tm);
+      case 128: return launch_all<128, fp8_t>(a, tm);
+    }
+  } else if (a.dtype == 0) {
     switch (a.geo.d) {
       case 32: return launch_all<32, float>(a, tm);
       case 64: return launch_all<64, float>(a, tm);

@@ -61,7 +61,7 @@ struct LaunchArgs {
   float2* rope;       // scratch: RoPE table
   float* partial;     // scratch: [heads][nseg*cps1][d*d + d]
   float* states;      // scratch: [nseg][heads][d*d + d]
-  bool bf16;
+  int dtype;          // GLA_DTYPE_* of q, k, v, g, beta, out
   hipStream_t stream;
   Geometry geo;
 };

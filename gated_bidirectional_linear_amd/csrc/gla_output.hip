@@ -6,8 +6,11 @@ namespace gla {
 // ===========================================================================
 // 4. Fused output
 // ===========================================================================
+// E is the tensor element type; the rotated queries go to LDS and into the
+// MFMA as Elem<E>::Lds (fp32 for fp32, bf16 for bf16 and fp8).
 template <int D, typename E>
 struct OutputCfg {
+  typedef typename Elem<E>::Lds L;
   static constexpr int CG = D / 8;
   static constexpr int TG = kThreads / CG;
   // 32-token tiles where every thread still has a whole token (d >= 64):
@@ -20,9 +23,9 @@ struct OutputCfg {
   static constexpr int PAIRS = MT * NTK;
   static constexpr int PPW = PAIRS >= 4 ? PAIRS / 4 : 1;   // (v tile, token tile) pairs per wave
   static constexpr int ACTIVE = PAIRS >= 4 ? 4 : PAIRS;    // waves with MFMA work
-  static constexpr int RQ_PITCH = D + (Elem<E>::is_bf16 ? 8 : 4);  // elements
+  static constexpr int RQ_PITCH = D + (Elem<L>::is_bf16 ? 8 : 4);  // elements
   static constexpr int NUM_PITCH = D + 4;                           // floats
-  static constexpr int RQ_BYTES = TILE * RQ_PITCH * (int)sizeof(E);
+  static constexpr int RQ_BYTES = TILE * RQ_PITCH * (int)sizeof(L);
   static constexpr int NUM_BYTES = TILE * NUM_PITCH * 4;
   static constexpr int SMEM = RQ_BYTES + NUM_BYTES;   // separate regions: two barriers per tile
 };
@@ -39,7 +42,8 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ rms_w, const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
   using C = OutputCfg<D, E>;
-  using M = Mfma<E>;
+  using L = typename C::L;
+  using M = Mfma<L>;
   using R = Rope<D>;
   using BR = BufRow<E>;
   typedef typename BR::Raw Raw;
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   constexpr bool kBf16 = Elem<E>::is_bf16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
   constexpr int kT = C::TILE;
-  E* rqs = reinterpret_cast<E*>(smem);                          // [kT][RQ_PITCH]  (token, k channel)
+  L* rqs = reinterpret_cast<L*>(smem);                          // [kT][RQ_PITCH]  (token, k channel)
   float* nums = reinterpret_cast<float*>(smem + C::RQ_BYTES);   // [kT][NUM_PITCH] (token, v channel)
 
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -173,9 +177,9 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
       rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * r);   // v_rcp_f32, 1 ulp
       R::apply(ph, cs[i]);
-      E* dst = rqs + (tg * C::TPT + i) * C::RQ_PITCH + 8 * cg;
-      if constexpr (kBf16) {
-        *reinterpret_cast<u32x4*>(dst) = Elem<E>::pack(ph);
+      L* dst = rqs + (tg * C::TPT + i) * C::RQ_PITCH + 8 * cg;
+      if constexpr (Elem<L>::is_bf16) {
+        *reinterpret_cast<u32x4*>(dst) = Elem<bf16_t>::pack(ph);
       } else {
         *reinterpret_cast<f32x4*>(dst) = (f32x4){ph[0], ph[1], ph[2], ph[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){ph[4], ph[5], ph[6], ph[7]};
@@ -267,6 +271,34 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
 // output_kernel.
 // ===========================================================================
 namespace pair2 {
+// 8 channels of one token as the kernel reads and writes them: bf16 rows
+// are 16 bytes, fp8 rows 8 bytes widened to bf16 words right before use
+// (every e4m3 value is exact in bf16).
+template <typename E> struct Row8;
+template <> struct Row8<bf16_t> {
+  static constexpr uint32_t ES = 2;
+  typedef u32x4 Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) { return buf_load16(r, voff, 0); }
+  __device__ __forceinline__ static u32x4 bf16x8(const Raw& u) { return u; }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, const float (&y)[8]) {
+    buf_store16(r, voff, 0, Elem<bf16_t>::pack(y));
+  }
+};
+template <> struct Row8<fp8_t> {
+  static constexpr uint32_t ES = 1;
+  typedef u32x2 Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return BufRow<fp8_t>::load(r, voff, 0);
+  }
+  __device__ __forceinline__ static u32x4 bf16x8(const Raw& u) {
+    return (u32x4){Elem<fp8_t>::bf16_pair<false>(u.x), Elem<fp8_t>::bf16_pair<true>(u.x),
+                   Elem<fp8_t>::bf16_pair<false>(u.y), Elem<fp8_t>::bf16_pair<true>(u.y)};
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, const float (&y)[8]) {
+    BufRow<fp8_t>::store(r, voff, 0, Elem<fp8_t>::pack(y));
+  }
+};
+
 constexpr int D = 128;
 constexpr int HP = 2;                 // heads per workgroup
 constexpr int TILE = 32;              // tokens per tile
@@ -280,10 +312,13 @@ constexpr int NUM_BYTES = TILE * HP * NUM_PITCH * 4;
 constexpr int KSTEPS = D / 16;
 }  // namespace pair2
 
+template <typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void output_pair_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ g, const float* __restrict__ states,
-    const float* __restrict__ rms_w, const float2* __restrict__ rope, bf16_t* __restrict__ out, Geometry G) {
+    const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
+    const float* __restrict__ rms_w, const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
   using namespace pair2;
+  using IO = Row8<E>;
+  constexpr uint32_t ES = IO::ES;
   using R = Rope<D>;
   using M = Mfma<bf16_t>;
   constexpr int SZ = D * D + D;
@@ -313,8 +348,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const uint32_t ROW = (uint32_t)G.heads * D * 2;
-  const uint32_t pair_off = (uint32_t)h0 * D * 2;
+  const uint32_t ROW = (uint32_t)G.heads * D * ES;
+  const uint32_t pair_off = (uint32_t)h0 * D * ES;
   auto tile_rsrc = [&](const void* p, long t0) {
     const long left = cend - t0;
     const uint32_t rows = left <= 0 ? 0u : (left >= TILE ? (uint32_t)TILE : (uint32_t)left);
@@ -323,7 +358,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   uint32_t voff[TPT];
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + tg) * ROW + (uint32_t)hl * D * 2 + 16u * c16;
+  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + tg) * ROW + (uint32_t)hl * D * ES + 8u * ES * c16;
 
   // this wave's head and its two 32-row tiles of S as A-fragments
   const int hw = wave >> 1;
@@ -363,16 +398,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
   const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
 
-  u32x4 qr[DEPTH][TPT], gr[DEPTH][TPT];
-  auto issue_q = [&](u32x4 (&r)[TPT], long t0) {
+  typedef typename IO::Raw Raw;
+  Raw qr[DEPTH][TPT], gr[DEPTH][TPT];
+  auto issue_q = [&](Raw (&r)[TPT], long t0) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+    for (int i = 0; i < TPT; ++i) r[i] = IO::load(rs, voff[i]);
   };
-  auto issue_g = [&](u32x4 (&r)[TPT], long t0) {
+  auto issue_g = [&](Raw (&r)[TPT], long t0) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, t0);
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+    for (int i = 0; i < TPT; ++i) r[i] = IO::load(rs, voff[i]);
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
@@ -384,7 +420,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // One tile.  Every path issues the same memory operations (rows past the
   // chunk read as zero, their stores are dropped), so the compiler's waits
   // cover exactly the rows in use.
-  auto tile = [&](u32x4 (&qt)[TPT], u32x4 (&gt)[TPT], long t0) {
+  auto tile = [&](Raw (&qt)[TPT], Raw (&gt)[TPT], long t0) {
     float rden[TPT];
     GridPos pp = pos;
 #pragma unroll
@@ -398,7 +434,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
       pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
 
-      const u32x4 u = qt[i];
+      const u32x4 u = IO::bf16x8(qt[i]);
       float ss = dot2sq(u.x, 0.f);
       ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
       const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
@@ -448,7 +484,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
       float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       float gv[8];
-      Elem<bf16_t>::unpack(gt[i], gv);
+      Elem<bf16_t>::unpack(IO::bf16x8(gt[i]), gv);
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
-      buf_store16(ors, voff[i], 0, Elem<bf16_t>::pack(y));   // rows past the chunk are dropped
+      IO::store(ors, voff[i], y);   // rows past the chunk are dropped
     }
     issue_g(gt, t0 + DEPTH * TILE);   // g rows consumed: refill DEPTH tiles ahead
   };
@@ -476,9 +512,9 @@ hipError_t launch_output(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   if constexpr (D == 128 && Elem<E>::is_bf16) {
     if (G.pass2_pair) {   // the planner sets it only for an even head count with the RoPE rows in LDS
-      hipLaunchKernelGGL(output_pair_kernel, dim3((G.heads / 2) * G.nseg * G.cps2), dim3(kThreads), 0, a.stream,
-                         (const bf16_t*)a.q, (const bf16_t*)a.g, (const float*)a.states, a.rms_w,
-                         (const float2*)a.rope, (bf16_t*)a.out, G);
+      hipLaunchKernelGGL((output_pair_kernel<E>), dim3((G.heads / 2) * G.nseg * G.cps2), dim3(kThreads), 0, a.stream,
+                         (const E*)a.q, (const E*)a.g, (const float*)a.states, a.rms_w,
+                         (const float2*)a.rope, (E*)a.out, G);
       return hipGetLastError();
     }
   }
@@ -498,5 +534,8 @@ template hipError_t launch_output<128, float>(const LaunchArgs&);
 template hipError_t launch_output<32, bf16_t>(const LaunchArgs&);
 template hipError_t launch_output<64, bf16_t>(const LaunchArgs&);
 template hipError_t launch_output<128, bf16_t>(const LaunchArgs&);
+template hipError_t launch_output<32, fp8_t>(const LaunchArgs&);
+template hipError_t launch_output<64, fp8_t>(const LaunchArgs&);
+template hipError_t launch_output<128, fp8_t>(const LaunchArgs&);
 
 }  // namespace gla

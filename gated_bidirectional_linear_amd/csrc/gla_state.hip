@@ -6,16 +6,19 @@ namespace gla {
 // ===========================================================================
 // 2. State partials: S_p = V_p^T (beta R phi K^)_p and z_p = sum phi K^
 // ===========================================================================
+// E is the tensor element type; operands are staged in LDS and fed to the
+// MFMA as Elem<E>::Lds (fp32 for fp32, bf16 for bf16 and fp8).
 template <int D, typename E>
 struct PartialCfg {
+  typedef typename Elem<E>::Lds L;
   static constexpr int CG = D / 8;                 // threads per token (8 channels each)
   static constexpr int TG = kThreads / CG;         // token groups
   static constexpr int TPT = kTile / TG;           // tokens per thread per tile
   static constexpr int MT = D / 32;                // 32-row MFMA tiles per dim
   static constexpr bool KSPLIT = MT * MT < 4;      // too few output tiles: waves split K
   static constexpr int TPW = KSPLIT ? 1 : MT * MT / 4;   // output tiles per wave
-  static constexpr int PITCH = kTile + (Elem<E>::is_bf16 ? 8 : 2);  // LDS row pitch (elements)
-  static constexpr int STAGE_BYTES = 2 * D * PITCH * (int)sizeof(E);
+  static constexpr int PITCH = kTile + (Elem<L>::is_bf16 ? 8 : 2);  // LDS row pitch (elements)
+  static constexpr int STAGE_BYTES = 2 * D * PITCH * (int)sizeof(L);
   static constexpr int ZRED_BYTES = TG * D * 4;
   static constexpr int KRED_BYTES = KSPLIT ? 4 * 64 * 16 * 4 : 0;
   static constexpr int SMEM = STAGE_BYTES > ZRED_BYTES ? (STAGE_BYTES > KRED_BYTES ? STAGE_BYTES : KRED_BYTES)
@@ -52,11 +55,12 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   using C = PartialCfg<D, E>;
-  using M = Mfma<E>;
+  using L = typename C::L;
+  using M = Mfma<L>;
   constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
-  E* rkT = reinterpret_cast<E*>(smem);          // [D][PITCH]  (k channel, token)
-  E* vT = rkT + D * C::PITCH;                   // [D][PITCH]  (v channel, token)
+  L* rkT = reinterpret_cast<L*>(smem);          // [D][PITCH]  (k channel, token)
+  L* vT = rkT + D * C::PITCH;                   // [D][PITCH]  (v channel, token)
 
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps1, G.chunk1);
@@ -135,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     const int col = tg * C::TPT;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      store_tcol<E, C::TPT>(rkT + (8 * cg + c) * C::PITCH + col, kx, c);
-      store_tcol<E, C::TPT>(vT + (8 * cg + c) * C::PITCH + col, vx, c);
+      store_tcol<L, C::TPT>(rkT + (8 * cg + c) * C::PITCH + col, kx, c);
+      store_tcol<L, C::TPT>(vT + (8 * cg + c) * C::PITCH + col, vx, c);
     }
     lds_barrier();
 
@@ -260,15 +264,53 @@ constexpr int kOffBits = 10;                   // packed table row offset (16-by
 constexpr int kRotBytes = kRopeLdsEntries * 8; // LDS rotation table
 using R = Rope<D>;
 
+// Streaming loads carry the nontemporal hint (bit 1 of the cache-policy
+// operand): every row is read once.
+constexpr int kStreamPolicy = 2;
+
+// The tensor element type seen by the bf16 code: 4 channels of one token as
+// two bf16 words.  fp8 rows are loaded as 4 bytes and widened right before
+// use (every e4m3 value is exact in bf16).
+template <typename E> struct Io;
+template <> struct Io<bf16_t> {
+  static constexpr uint32_t ES = 2;   // bytes per element
+  typedef u32x2 Word;                 // 4 channels as loaded
+  __device__ __forceinline__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kStreamPolicy));
+  }
+  __device__ __forceinline__ static u32x2 bf16x4(Word w) { return w; }
+  __device__ __forceinline__ static uint32_t load_beta(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static int beta_f32_bits(uint32_t b) { return (int)(b << 16); }
+};
+template <> struct Io<fp8_t> {
+  static constexpr uint32_t ES = 1;
+  typedef uint32_t Word;
+  __device__ __forceinline__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kStreamPolicy);
+  }
+  __device__ __forceinline__ static u32x2 bf16x4(Word w) {
+    return (u32x2){Elem<fp8_t>::bf16_pair<false>(w), Elem<fp8_t>::bf16_pair<true>(w)};
+  }
+  __device__ __forceinline__ static uint32_t load_beta(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static int beta_f32_bits(uint32_t b) {
+    return __float_as_int(__builtin_amdgcn_cvt_f32_fp8((int)b, 0));
+  }
+};
+
+template <typename E>
 struct Rows {
-  u32x2 k[8], v[8];
-  uint32_t b;               // beta (bf16 bits) of this lane's own token
+  typename Io<E>::Word k[8], v[8];
+  uint32_t b;               // beta (raw bits) of this lane's own token
 };
 
 // Per-lane constants of a chunk.
 struct Lane {
   int lane, m, h;
-  uint32_t lane_off;        // byte offset of this lane's 8 bytes in a step's row 8h
+  uint32_t lane_off;        // byte offset of this lane's 4 channels in a step's row 8h
   uint32_t beta_off;        // byte offset of beta of this lane's own token in a step
   uint32_t ROW;             // bytes between tokens
   uint32_t lane_rel;        // this lane's pair offset inside a table row (16-byte units)
@@ -276,14 +318,16 @@ struct Lane {
   int t_lo, t_last, nt;     // frames the chunk spans
 };
 
+template <typename E>
 __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
+  constexpr uint32_t ES = Io<E>::ES;
   Lane L;
   L.lane = threadIdx.x & 63;
   L.m = L.lane & 31;
   L.h = L.lane >> 5;
-  L.ROW = (uint32_t)G.heads * D * 2;
-  L.lane_off = (uint32_t)(8 * L.h) * L.ROW + (uint32_t)ch.head * D * 2 + 8u * L.m;
-  L.beta_off = ((uint32_t)(8 * L.h + (L.lane & 7)) * (uint32_t)G.heads + (uint32_t)ch.head) * 2;
+  L.ROW = (uint32_t)G.heads * D * ES;
+  L.lane_off = (uint32_t)(8 * L.h) * L.ROW + (uint32_t)ch.head * D * ES + 4u * ES * L.m;
+  L.beta_off = ((uint32_t)(8 * L.h + (L.lane & 7)) * (uint32_t)G.heads + (uint32_t)ch.head) * ES;
   // pairs 2m and 2m+1 share an axis
   const int axis = (2 * L.m < R::PT) ? 0 : ((2 * L.m < R::PT + R::PY) ? 1 : 2);
   const int first = axis == 0 ? 0 : (axis == 1 ? R::PT : R::PT + R::PY);
@@ -327,12 +371,6 @@ __device__ __forceinline__ uint32_t sel_channel(u32x2 ra, u32x2 rb, int c) {
   return (c & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u) : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
 }
 
-// Streaming loads carry the nontemporal hint (bit 1 of the cache-policy
-// operand): every row is read once.
-constexpr int kStreamPolicy = 2;
-__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kStreamPolicy));
-}
 
 // sum of the two bf16 products a.lo*b.lo + a.hi*b.hi, accumulated in fp32
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
@@ -340,21 +378,22 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
 }
 
 // Rows [base, base + 16) of a step; rows at or past `end` read as zero.
-__device__ __forceinline__ void issue(Rows& r, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                      const bf16_t* __restrict__ beta, long base, long end, int heads,
+template <typename E>
+__device__ __forceinline__ void issue(Rows<E>& r, const E* __restrict__ k, const E* __restrict__ v,
+                                      const E* __restrict__ beta, long base, long end, int heads,
                                       const Lane& L) {
   const long left = end - base;
   const uint32_t nvalid = left <= 0 ? 0u : (left >= kStep ? (uint32_t)kStep : (uint32_t)left);
   const size_t row0 = (size_t)base * heads * D;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + row0, nvalid * L.ROW);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + row0, nvalid * L.ROW);
-  const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + (size_t)base * heads, nvalid * (uint32_t)heads * 2);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(beta + (size_t)base * heads, nvalid * (uint32_t)heads * Io<E>::ES);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    r.k[i] = ld8(krs, L.lane_off + (uint32_t)i * L.ROW);
-    r.v[i] = ld8(vrs, L.lane_off + (uint32_t)i * L.ROW);
+    r.k[i] = Io<E>::load(krs, L.lane_off + (uint32_t)i * L.ROW);
+    r.v[i] = Io<E>::load(vrs, L.lane_off + (uint32_t)i * L.ROW);
   }
-  r.b = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, (int)L.beta_off, 0, 0);
+  r.b = Io<E>::load_beta(brs, L.beta_off);
 }
 
 // Table row offsets (16-byte units) of the token at `gp` on the three axes.
@@ -389,11 +428,18 @@ __device__ __forceinline__ float pair_rows_sum(float x) {
 struct NoWork {
   __device__ __forceinline__ void operator()(int) const {}
 };
-template <typename Between = NoWork>
-__device__ __forceinline__ void build_step(const Rows& r, uint32_t offs, const unsigned char* rtab, const Lane& L,
+template <typename E, typename Between = NoWork>
+__device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, const unsigned char* rtab, const Lane& L,
                                            float eps, float (&zacc)[4], u32x4 (&kf)[4], u32x4 (&vf)[4],
                                            Between between = Between()) {
-  const int bsrc = (int)(r.b << 16);
+  // 4 channels of each of the 8 tokens as bf16 words
+  struct { u32x2 k[8], v[8]; } r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    r.k[i] = Io<E>::bf16x4(raw.k[i]);
+    r.v[i] = Io<E>::bf16x4(raw.v[i]);
+  }
+  const int bsrc = Io<E>::beta_f32_bits(raw.b);
   // rotation words of the 8 tokens: all table reads issued together
   u32x4 cs[8];
   float bt[8];
@@ -479,8 +525,9 @@ constexpr int kSumBytes = 4 * kHalfBytes;    // the 4 waves' halves during the f
 constexpr int kDepth = GLA_ACC_DEPTH;        // steps of rows in flight per wave
 }  // namespace acc1
 
+template <typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_partial_acc_kernel(
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ beta,
+    const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   using namespace frag1;
   using namespace acc1;
@@ -492,7 +539,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps1, G.chunk1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const Lane L = make_lane(G, ch);
+  const Lane L = make_lane<E>(G, ch);
   const int HW = G.H * G.W;
   stage_rotations(rtab, rope, G, L);
 
@@ -529,7 +576,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // refills its rows and the loop body runs all kDepth steps, also past the
   // chunk end (those rows read as zero and add nothing): with the same loads
   // on every path the compiler waits for exactly the rows a step uses.
-  auto step = [&](Rows& rows, long t0) {
+  auto step = [&](Rows<E>& rows, long t0) {
     u32x4 kf[4], vf[4];
     build_step(rows, table_rows(gp, L, G.H), rtab, L, G.eps, zacc, kf, vf, mfma_row);
     gp.advance(adt, ady, adx, G.H, G.W);
@@ -541,7 +588,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  Rows rr[kDepth];
+  Rows<E> rr[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(rr[d], k, v, beta, ch.begin + d * kTile + wave * kStep, ch.end, G.heads, L);
   for (long t0 = ch.begin; t0 < ch.end; t0 += kDepth * kTile) {
@@ -588,10 +635,10 @@ template <int D, typename E>
 hipError_t launch_state_partial(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   const int blocks = G.heads * G.nseg * G.cps1;
-  if constexpr (D == 128 && Elem<E>::is_bf16) {
+  if constexpr (D == 128 && Elem<typename Elem<E>::Lds>::is_bf16) {   // bf16 and fp8 rows
     if (G.pass1_reg) {   // the planner sets it only with the RoPE rows in LDS
-      hipLaunchKernelGGL(state_partial_acc_kernel, dim3(blocks), dim3(kThreads), 0, a.stream, (const bf16_t*)a.k,
-                         (const bf16_t*)a.v, (const bf16_t*)a.beta, (const float2*)a.rope, a.partial, G);
+      hipLaunchKernelGGL((state_partial_acc_kernel<E>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.k,
+                         (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
       return hipGetLastError();
     }
   }
@@ -610,5 +657,8 @@ template hipError_t launch_state_partial<128, float>(const LaunchArgs&);
 template hipError_t launch_state_partial<32, bf16_t>(const LaunchArgs&);
 template hipError_t launch_state_partial<64, bf16_t>(const LaunchArgs&);
 template hipError_t launch_state_partial<128, bf16_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<32, fp8_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<64, fp8_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<128, fp8_t>(const LaunchArgs&);
 
 }  // namespace gla

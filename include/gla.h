@@ -59,8 +59,14 @@ typedef enum {
 } gla_status;
 
 typedef enum {
-  GLA_DTYPE_F32 = 0,   /* q, k, v, g, beta, out are float32 */
-  GLA_DTYPE_BF16 = 1   /* q, k, v, g, beta, out are bfloat16 (fp32 accumulation inside) */
+  GLA_DTYPE_F32 = 0,      /* q, k, v, g, beta, out are float32 */
+  GLA_DTYPE_BF16 = 1,     /* q, k, v, g, beta, out are bfloat16 (fp32 accumulation inside) */
+  GLA_DTYPE_FP8_E4M3 = 2  /* q, k, v, g, beta, out are OCP FP8 E4M3 (e4m3fn: bias 7, max 448,
+                             no infinities), one byte each; the state, the denominators and all
+                             accumulation stay fp32 and the output is rounded to nearest even.
+                             Low-precision operator I/O halves the bytes of a bandwidth-bound
+                             op (SANA-Video 2.0 digest, weaknesses: the attention operator stays
+                             BF16, so quantisation of the linear GEMMs alone saves only 5.8%). */
 } gla_dtype;
 
 /*

@@ -4,13 +4,13 @@ from __future__ import annotations
 
 import numpy as np
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}   # max|err| <= TOL * max|ref|
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 2e-2}   # max|err| <= TOL * max|ref| (fp8: beyond output rounding)
 
 # Key-sum state z.  For bf16 inputs the HIP path multiplies each token's phi(k)
 # by its RMS factor rounded to bf16 (relative error <= 2^-9); every term of z
 # is non-negative, so each channel's sum keeps that relative bound.  fp32
 # accumulation over the sequence adds far less.
-Z_TOL = {"f32": 1e-5, "bf16": 2.5e-3}
+Z_TOL = {"f32": 1e-5, "bf16": 2.5e-3, "fp8": 2.5e-3}   # fp8 at d = 128 runs the bf16 fast pass 1 too
 
 
 def torch_mod():
@@ -27,13 +27,16 @@ def gpu_available() -> bool:
 
 
 def to_device(inp: dict, device="cuda"):
-    """Upload a make_inputs() dict: bf16 from its exact bits, f32 as is."""
+    """Upload a make_inputs() dict: bf16 and fp8 from their exact bits, f32 as is."""
     torch = torch_mod()
     out = {}
     for name in ("q", "k", "v", "g", "beta"):
         if inp["dtype"] == "bf16":
             bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
             out[name] = torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        elif inp["dtype"] == "fp8":
+            bits = np.ascontiguousarray(inp[name + "_bits"], dtype=np.uint8)
+            out[name] = torch.from_numpy(bits).to(device).view(torch.float8_e4m3fn)
         else:
             out[name] = torch.from_numpy(np.ascontiguousarray(inp[name])).to(device)
     out["rms_w"] = torch.from_numpy(np.ascontiguousarray(inp["rms_w"], dtype=np.float32)).to(device)
@@ -42,7 +45,24 @@ def to_device(inp: dict, device="cuda"):
 
 def to_f64(t) -> np.ndarray:
     torch = torch_mod()
+    if t.dtype == torch.float8_e4m3fn:   # decoded by the generator's own codec
+        from workloads import fp8_bits_to_f32
+        return fp8_bits_to_f32(t.detach().view(torch.uint8).cpu().numpy()).astype(np.float64)
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+def fp8_excess(got, ref) -> float:
+    """Error of an FP8 E4M3 output beyond its own rounding, relative to max|ref|:
+    max(|got - ref| - 2^-4 |ref| - 2^-10) / max|ref|.  Rounding to nearest
+    costs at most 2^-4 |x| for normal values and 2^-10 below 2^-6; what is
+    left is the path's internal error, held to the bf16 tolerance."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = float(np.max(np.abs(ref)))
+    ex = np.abs(got - ref) - 2.0 ** -4 * np.abs(ref) - 2.0 ** -10
+    return max(0.0, float(np.max(ex))) / (den if den > 0 else 1.0)
 
 
 def rel_err(got, ref) -> float:

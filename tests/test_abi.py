@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
-    assert lib.gla_version() & 0xFFFF >= 1          # 1.1: gla_block_causal_forward_at
+    assert lib.gla_version() & 0xFFFF >= 2          # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
@@ -82,8 +82,11 @@ def test_frame_offset_errors(lib):
 
 
 def test_dtype_and_head_dim_errors(lib):
-    assert fwd(lib, dtype=2) == E_DTYPE
+    assert fwd(lib, dtype=3) == E_DTYPE          # 0 fp32, 1 bf16, 2 fp8 e4m3 are the known codes
     assert fwd(lib, dtype=-1) == E_DTYPE
+    for dt in (0, 1, 2):                          # known dtypes reach the later checks
+        assert fwd(lib, dtype=dt, d=48) == E_D
+        assert fwd(lib, dtype=dt, heads=0) == E_SHAPE
     for d in (0, 16, 48, 96, 256):
         assert fwd(lib, d=d) == E_D
         assert bc(lib, d=d) == E_D

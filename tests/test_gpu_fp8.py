@@ -1,0 +1,96 @@
+"""GPU parity of the FP8 E4M3 operator I/O (q, k, v, g, beta and out in OCP
+e4m3fn; fp32 state and accumulation) against the fp64 oracle evaluated on the
+exact decoded fp8 inputs.  The output is compared beyond its own rounding:
+|got - ref| - 2^-4 |ref| - 2^-10 <= 2e-2 max|ref| (the bf16 tolerance for the
+path's internal error)."""
+import numpy as np
+import pytest
+
+import oracle.gla_oracle as orc
+from workloads import WORKLOADS, make_inputs, make_state
+from tests.gpu_helpers import TOL, Z_TOL, fp8_excess, rel_err, run_block_causal, run_forward, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, **kw):
+    return orc.gla_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"], inp["grid"],
+                           inp["eps"], **kw)
+
+
+def _oracle_bc(inp, F, S0=None, z0=None, **kw):
+    return orc.gla_block_causal_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"],
+                                        inp["grid"], inp["eps"], F, S0=S0, z0=z0, **kw)
+
+
+def _report(name, err):
+    print(f"[parity] fp8 {name}: error beyond output rounding {err:.3e} (tol {TOL['fp8']:.0e})", flush=True)
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 4, 2, 32), (1, 1, 1, 3, 64), (3, 5, 7, 2, 64), (5, 9, 13, 3, 128),
+                                   (4, 16, 16, 2, 128), (9, 15, 26, 2, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_shapes(shape):
+    T, H, W, heads, d = shape
+    print(f"[case] fp8 shape {shape}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=31)
+    out = run_forward(to_device(inp), inp["grid"], inp["eps"])
+    got = to_f64(out)
+    ref = _oracle(inp)
+    err = fp8_excess(got, ref)
+    _report(str(shape), err)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL["fp8"]
+
+
+def test_fp8_480p_workload():
+    w = WORKLOADS["480p"]
+    print(f"[case] fp8 {w.name}", flush=True)
+    inp = make_inputs(w.T, w.H, w.W, w.heads, w.d, "fp8", seed=0, eps=w.eps)
+    got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = fp8_excess(got, _oracle(inp))
+    _report(w.name, err)
+    assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("shape", [(7, 3, 5, 2, 64, 2), (9, 8, 9, 2, 128, 3)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_block_causal(shape):
+    T, H, W, heads, d, F = shape
+    print(f"[case] fp8 block-causal {shape}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=32)
+    S0, z0 = make_state(heads, d, seed=4)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F, S0, z0)
+    ro, rS, rz = _oracle_bc(inp, F, S0=S0, z0=z0)
+    err = fp8_excess(to_f64(out), ro)
+    _report(f"block-causal {shape}", err)
+    assert err <= TOL["fp8"]
+    assert rel_err(to_f64(S), rS) <= 1e-2
+    assert rel_err(to_f64(z), rz) <= Z_TOL["fp8"]
+
+
+def test_fp8_streamed_calls():
+    T, H, W, heads, d, F = 6, 5, 6, 2, 128, 2
+    hw = H * W
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=33)
+    outs, S, z = [], None, None
+    for t0, t1 in ((0, 2), (2, 6)):
+        part = {k: (v[t0 * hw: t1 * hw] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+        part["grid"] = (t1 - t0, H, W)
+        o, S_t, z_t = run_block_causal(to_device(part), part["grid"], part["eps"], F, S, z, t_offset=t0)
+        outs.append(to_f64(o))
+        S, z = S_t.cpu().numpy(), z_t.cpu().numpy()
+    ro, rS, rz = _oracle_bc(inp, F)
+    err = fp8_excess(np.concatenate(outs), ro)
+    _report("streamed", err)
+    assert err <= TOL["fp8"]
+    assert rel_err(S.astype(np.float64), rS) <= 1e-2
+
+
+def test_fp8_binding_rejects_mixed_dtypes():
+    torch = pytest.importorskip("torch")
+    import gated_bidirectional_linear_amd as gla
+    inp = make_inputs(2, 2, 2, 2, 32, "fp8", seed=34)
+    dev = to_device(inp)
+    dev["g"] = dev["g"].to(torch.bfloat16)
+    with pytest.raises(TypeError):
+        gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"])

@@ -30,6 +30,10 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "round_to_bf16",
+    "f32_to_fp8_bits",
+    "fp8_bits_to_f32",
+    "round_to_fp8",
+    "FP8_MAX",
 ]
 
 
@@ -49,10 +53,14 @@ class Workload:
     def N(self) -> int:
         return self.T * self.H * self.W
 
+    @property
+    def elem_size(self) -> int:
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
     def alg_bytes(self) -> int:
         """Algorithmic HBM bytes of one call: read q,k,v,g,beta, write out,
         plus read+write of the fp32 carried state in block-causal mode."""
-        s = 4 if self.dtype == "f32" else 2
+        s = self.elem_size
         b = 5 * self.N * self.heads * self.d * s + self.N * self.heads * s
         if self.block_frames is not None:
             b += 2 * self.heads * (self.d * self.d + self.d) * 4
@@ -101,6 +109,47 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(f32_to_bf16_bits(x))
 
 
+# OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+# exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; there are no
+# infinities and the largest finite value is 448 (S.1111.110).
+FP8_MAX = 448.0
+
+
+def fp8_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Decode FP8 E4M3 bits (uint8) to fp32 values."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int32)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
+
+
+def f32_to_fp8_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to FP8 E4M3, nearest with ties to even, saturating
+    magnitudes past 448 to 448; returns uint8 bits.  Inputs must not be NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int32)
+    # subnormal range (a < 2^-6): units of 2^-9; 8 units is the smallest normal (code 8)
+    sub = np.rint(a * 2.0 ** 9).astype(np.int64)
+    # normal range: a = f * 2^ex with f in [0.5, 1), exponent e = ex - 1
+    f, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = ex.astype(np.int64) - 1
+    q = np.rint((2.0 * f - 1.0) * 8.0).astype(np.int64)   # 0..8 eighths above 1
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    norm = ((e + 7) << 3) | q
+    code = np.where(a < 2.0 ** -6, sub, norm)
+    code = np.where(a >= FP8_MAX, 0x7E, np.minimum(code, 0x7E))
+    return (code.astype(np.int32) | sign).astype(np.uint8)
+
+
+def round_to_fp8(x: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest FP8 E4M3 value, returned as fp32."""
+    return fp8_bits_to_f32(f32_to_fp8_bits(x))
+
+
 _BLOCK = 1 << 22          # elements per independently seeded block
 _STREAMS = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "rms_w": 5}
 
@@ -122,7 +171,8 @@ def _workers() -> int:
 def _draw(seed: int, name: str, shape, dtype: str, keep_f32: bool, pool, sigmoid: bool = False):
     size = int(np.prod(shape))
     f32 = np.empty(size, np.float32) if (keep_f32 or dtype == "f32") else None
-    bits = np.empty(size, np.uint16) if dtype == "bf16" else None
+    bits = np.empty(size, {"bf16": np.uint16, "fp8": np.uint8}[dtype]) if dtype != "f32" else None
+    encode, decode = (f32_to_fp8_bits, fp8_bits_to_f32) if dtype == "fp8" else (f32_to_bf16_bits, bf16_bits_to_f32)
     stream = _STREAMS[name]
 
     def work(b):
@@ -132,10 +182,10 @@ def _draw(seed: int, name: str, shape, dtype: str, keep_f32: bool, pool, sigmoid
         if sigmoid:
             x = (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
         if bits is not None:
-            bb = f32_to_bf16_bits(x)
+            bb = encode(x)
             bits[lo:hi] = bb
             if f32 is not None:
-                f32[lo:hi] = bf16_bits_to_f32(bb)
+                f32[lo:hi] = decode(bb)
         else:
             f32[lo:hi] = x
 
@@ -154,16 +204,17 @@ def make_inputs(T: int, H: int, W: int, heads: int, d: int, dtype: str, seed: in
 
     Returns a dict with fp32 numpy arrays ``q, k, v, g`` of shape [N, heads, d],
     ``beta`` [N, heads], ``rms_w`` [d], plus ``eps``, ``grid`` (T, H, W) and
-    ``dtype``.  For dtype "bf16" the fp32 arrays hold exactly the bf16 values
-    the operator receives, and ``*_bits`` (uint16) hold their storage;
-    with keep_f32=False only the bits are kept (large workloads).
+    ``dtype``.  For dtype "bf16" ("fp8") the fp32 arrays hold exactly the bf16
+    (FP8 E4M3) values the operator receives, and ``*_bits`` (uint16, uint8)
+    hold their storage; with keep_f32=False only the bits are kept (large
+    workloads).
 
     Each tensor is filled in row-major order in blocks of 2^22 elements; block
     b of tensor t (q, k, v, g, beta-logit, rms_w-noise = 0..5) is drawn from
     PCG64(SeedSequence(seed, spawn_key=(t, b))), so the values do not depend
     on how many threads draw them.
     """
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "fp8"):
         raise ValueError(f"unknown dtype {dtype!r}")
     N = T * H * W
     from concurrent.futures import ThreadPoolExecutor
@@ -196,11 +247,12 @@ def make_workload_inputs(w: Workload, seed: int = 0, keep_f32: bool = True) -> d
 
 
 def head_slice_f32(inp: dict, heads) -> dict:
-    """fp32 copies of the listed heads of a bits-only bf16 input set."""
+    """fp32 copies of the listed heads of a bits-only bf16 or fp8 input set."""
     out = dict(inp)
+    decode = fp8_bits_to_f32 if inp["dtype"] == "fp8" else bf16_bits_to_f32
     for name in ("q", "k", "v", "g"):
-        out[name] = bf16_bits_to_f32(inp[name + "_bits"][:, heads, :])
-    out["beta"] = bf16_bits_to_f32(inp["beta_bits"][:, heads])
+        out[name] = decode(inp[name + "_bits"][:, heads, :])
+    out["beta"] = decode(inp["beta_bits"][:, heads])
     return out
 
 
