@@ -271,9 +271,8 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
 // output_kernel.
 // ===========================================================================
 namespace pair2 {
-// 8 channels of one token as the kernel reads and writes them: bf16 rows
-// are 16 bytes, fp8 rows 8 bytes widened to bf16 words right before use
-// (every e4m3 value is exact in bf16).
+// 8 channels of one token as the kernel reads and writes them (bf16 rows of
+// 16 bytes).
 template <typename E> struct Row8;
 template <> struct Row8<bf16_t> {
   static constexpr uint32_t ES = 2;
@@ -282,20 +281,6 @@ template <> struct Row8<bf16_t> {
   __device__ __forceinline__ static u32x4 bf16x8(const Raw& u) { return u; }
   __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, const float (&y)[8]) {
     buf_store16(r, voff, 0, Elem<bf16_t>::pack(y));
-  }
-};
-template <> struct Row8<fp8_t> {
-  static constexpr uint32_t ES = 1;
-  typedef u32x2 Raw;
-  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return BufRow<fp8_t>::load(r, voff, 0);
-  }
-  __device__ __forceinline__ static u32x4 bf16x8(const Raw& u) {
-    return (u32x4){Elem<fp8_t>::bf16_pair<false>(u.x), Elem<fp8_t>::bf16_pair<true>(u.x),
-                   Elem<fp8_t>::bf16_pair<false>(u.y), Elem<fp8_t>::bf16_pair<true>(u.y)};
-  }
-  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, const float (&y)[8]) {
-    BufRow<fp8_t>::store(r, voff, 0, Elem<fp8_t>::pack(y));
   }
 };
 
