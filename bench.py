@@ -106,7 +106,7 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
     # every launch of a pass (whichever of its kernel variants ran) is summarised
     # under the timing name of that pass
     for prefix, short in (("gla::output", "output_kernel"), ("gla::state_partial", "state_partial_kernel")):
-        names = [k for k in fetch if k.startswith(prefix) and k not in copy]
+        names = [k for k in fetch if k.removeprefix("void ").startswith(prefix) and k not in copy]
         if not names:
             continue
         kn = names[0]
@@ -118,7 +118,7 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
             f.write("# commands:\n")
             for line in commands.strip().splitlines():
                 f.write(f"#   {line}\n")
-            f.write(f"kernel: {kn.split('(')[0]}\n")
+            f.write(f"kernel: {kn.removeprefix('void ').split('(')[0]}\n")
             f.write(f"FETCH_SIZE_kib_per_dispatch: {fetch[kn]:.1f}\n")
             f.write(f"WRITE_SIZE_kib_per_dispatch: {write.get(kn, 0.0):.1f}\n")
             f.write(f"copy_calibration: {ck.split('(')[0]} of {calib_mib} MiB read + {calib_mib} MiB written; "
