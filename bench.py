@@ -190,7 +190,7 @@ def main(argv=None):
                     help="operator I/O dtype (default: the workload's own, bf16 for 720p_60s); "
                          "fp8 = OCP FP8 E4M3 q, k, v, g, beta and out")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-heads", type=int, default=6, help="heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run 3 elementwise copies (torch.neg, fp32) reading and "
