@@ -24,6 +24,9 @@ What it computes (per head, tokens n, j of one video-latent grid):
   latent frames (notes, key design 2: cumulative state + key sum form a
   constant-memory cache).  Tokens of block b see blocks <= b; inside a block
   attention is bidirectional.
+* Token-causal mode: token i sees the tokens before it in row-major order
+  (notes, key design 2: the causal form as running sums up to i - 1), or
+  also itself; both readings are evaluated.
 
 Readings where the pages are silent (each listed with its reason in the
 design notes of the repository):
@@ -55,6 +58,7 @@ __all__ = [
     "head_features",
     "gla_forward",
     "gla_block_causal_forward",
+    "gla_token_causal_forward",
     "block_bounds",
 ]
 
@@ -229,3 +233,52 @@ def gla_block_causal_forward(q, k, v, beta, g, rms_w, grid, eps, block_frames, S
     if not return_parts:
         return out, S_fin, z_fin
     return {"out": out, "S": S_fin, "z": z_fin, "block_states": block_states}
+
+
+def gla_token_causal_forward(q, k, v, beta, g, rms_w, grid, eps, include_self=True, S0=None, z0=None,
+                             rope=True, return_parts=False, pos_offset=(0, 0, 0)):
+    """Token-level causal operator (SANA-Video notes, key design 2: causal
+    linear attention as running sums of the per-token states and key sums).
+
+    Tokens are taken in row-major (t, y, x) order.  Token i reads the carried
+    state (S0, z0) plus the tokens j <= i (include_self) or j < i (strictly
+    earlier, the notes' sums up to i - 1).  Written as masked kernel attention
+    with M_ij = [j <= i] (or [j < i]):
+        num_i = S0 rq_i + sum_j M_ij beta_j (rk_j . rq_i) v_j
+        den_i = phi(q_i) . (z0 + sum_j M_ij phi(k_j)) + eps
+        out_i = w * rmsnorm(sigmoid(g_i) * num_i / den_i)
+    The state after the call is S0 + sum_j beta_j v_j rk_j^T, z0 + sum_j phi(k_j).
+    Returns (out [N, heads, d], S_final, z_final), or a dict with num and den
+    as well when return_parts.  Dense N x N per head: for test sizes only.
+    """
+    T, H, W = grid
+    N = T * H * W
+    q = np.asarray(q)
+    nh, d = q.shape[1], q.shape[2]
+    ang = rope_angles(T, H, W, d, pos_offset=pos_offset) if rope else None
+    w = np.asarray(rms_w, dtype=np.float64)
+    mask = np.tril(np.ones((N, N)), 0 if include_self else -1)
+    out = np.zeros((N, nh, d))
+    nums = np.zeros((N, nh, d))
+    dens = np.zeros((N, nh))
+    S_fin = np.zeros((nh, d, d))
+    z_fin = np.zeros((nh, d))
+    for h in range(nh):
+        S = np.zeros((d, d)) if S0 is None else np.asarray(S0[h], dtype=np.float64)
+        z = np.zeros(d) if z0 is None else np.asarray(z0[h], dtype=np.float64)
+        pk, rk = head_features(_head(k, h), ang, eps)
+        pq, rq = head_features(_head(q, h), ang, eps)
+        bh = np.asarray(beta[:, h], dtype=np.float64)
+        vh = _head(v, h)
+        num = rq @ S.T + (mask * (rq @ rk.T) * bh[None, :]) @ vh
+        den = pq @ z + (mask * (pq @ pk.T)).sum(axis=1) + eps
+        x = sigmoid(_head(g, h)) * num / den[:, None]
+        out[:, h, :] = w[None, :] * rms_normalize(x, eps)
+        nums[:, h, :] = num
+        dens[:, h] = den
+        dS, dz = _state(bh, vh, pk, rk)
+        S_fin[h] = S + dS
+        z_fin[h] = z + dz
+    if not return_parts:
+        return out, S_fin, z_fin
+    return {"out": out, "S": S_fin, "z": z_fin, "num": nums, "den": dens}

@@ -43,10 +43,11 @@ def _rotation_matrix(t, y, x, d, base=10000.0, off=(0, 0, 0)):
 
 
 def brute_force(q, k, v, beta, g, w, grid, eps, rope=True, block_frames=None, S0=None, z0=None,
-                off=(0, 0, 0)):
+                off=(0, 0, 0), token_causal=None):
     """o_j = w * rmsnorm( sig(g_j) * sum_n A_jn v_n / (sum_n D_jn + eps) ), with
     A_jn = beta_n (R_j phi q_j).(R_n phi k_n), D_jn = phi q_j . phi k_n, and for the
-    block-causal form the mask blk(n) <= blk(j) plus the carried state."""
+    block-causal form the mask blk(n) <= blk(j) plus the carried state; for the
+    token-causal form ("incl" or "excl") the mask n <= j or n < j."""
     T, H, W = grid
     N, nh, d = q.shape
     toks = [(t, y, x) for t in range(T) for y in range(H) for x in range(W)]
@@ -67,6 +68,10 @@ def brute_force(q, k, v, beta, g, w, grid, eps, rope=True, block_frames=None, S0
         A = (rq @ rk.T) * beta[:, h].astype(np.float64)[None, :]
         D = pq @ pk.T
         M = (blk[None, :] <= blk[:, None]).astype(np.float64)
+        if token_causal is not None:
+            n_idx = np.arange(N)
+            M = ((n_idx[None, :] <= n_idx[:, None]) if token_causal == "incl"
+                 else (n_idx[None, :] < n_idx[:, None])).astype(np.float64)
         num = (A * M) @ v[:, h, :].astype(np.float64)
         den = (D * M).sum(axis=1) + eps
         if S0 is not None:
@@ -532,3 +537,87 @@ def _mut_dropped_beta(monkeypatch):
 def test_planted_state_mistake_is_caught(monkeypatch, mutant):
     mutant(monkeypatch)
     assert not _pins_pass()
+
+
+# ----------------------------------------------------------------------------
+# Token-causal pins
+# ----------------------------------------------------------------------------
+
+def _tc(inp, include_self=True, S0=None, z0=None, **kw):
+    return orc.gla_token_causal_forward(*_args(inp), include_self=include_self, S0=S0, z0=z0, **kw)
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+@pytest.mark.parametrize("grid", [(3, 2, 3), (2, 3, 2), (4, 1, 1)])
+def test_token_causal_matches_masked_brute_force(grid, include_self):
+    inp = _inputs(*grid, 2, 32, 51)
+    rng = np.random.default_rng(5)
+    S0 = rng.standard_normal((2, 32, 32))
+    z0 = np.abs(rng.standard_normal((2, 32)))
+    for s0, z0_ in ((None, None), (S0, z0)):
+        o, S, z = _tc(inp, include_self, s0, z0_, pos_offset=(3, 0, 0))
+        bo, _, _ = brute_force(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"],
+                               inp["rms_w"].astype(np.float64), grid, inp["eps"], S0=s0, z0=z0_,
+                               off=(3, 0, 0), token_causal="incl" if include_self else "excl")
+        assert _relerr(o, bo) < RTOL_EXACT
+
+
+def test_token_causal_one_token_frames_equal_block_causal():
+    """On a T x 1 x 1 grid every frame is one token: the inclusive token-causal
+    form is the block-causal form with one frame per block."""
+    inp = _inputs(9, 1, 1, 2, 32, 52)
+    o, S, z = _tc(inp, True)
+    ob, Sb, zb = _bc(inp, 1)
+    assert _relerr(o, ob) < RTOL_EXACT
+    assert _relerr(S, Sb) < RTOL_EXACT and _relerr(z, zb) < RTOL_EXACT
+    oe, _, _ = _tc(inp, False)        # the strict reading differs
+    assert _relerr(oe, ob) > 1e-3
+
+
+def test_token_causal_last_token_reads_everything():
+    """With the own token included, the last token sees the whole sequence:
+    its output is the bidirectional output there; the final state is the
+    bidirectional state."""
+    inp = _inputs(3, 2, 4, 2, 32, 53)
+    o, S, z = _tc(inp, True)
+    parts = orc.gla_forward(*_args(inp), return_parts=True)
+    assert _relerr(o[-1], parts["out"][-1]) < RTOL_EXACT
+    assert _relerr(S, parts["S"]) < RTOL_EXACT and _relerr(z, parts["z"]) < RTOL_EXACT
+
+
+def test_token_causal_first_token_strict_reads_nothing():
+    """Strictly earlier tokens only: token 0 has no numerator and den = eps, so
+    its output is exactly zero (with no carried state)."""
+    inp = _inputs(2, 2, 3, 2, 32, 54)
+    o, _, _ = _tc(inp, False)
+    assert np.all(o[0] == 0.0)
+    assert np.any(o[1] != 0.0)
+
+
+def test_token_causal_strict_is_inclusive_minus_own_term():
+    inp = _inputs(2, 3, 3, 2, 32, 55)
+    pi = _tc(inp, True, return_parts=True)
+    ps = _tc(inp, False, return_parts=True)
+    ang = orc.rope_angles(*inp["grid"], 32)
+    for h in range(2):
+        pk, rk = orc.head_features(np.asarray(inp["k"][:, h], np.float64), ang, inp["eps"])
+        pq, rq = orc.head_features(np.asarray(inp["q"][:, h], np.float64), ang, inp["eps"])
+        own = (np.sum(rq * rk, axis=1) * inp["beta"][:, h])[:, None] * inp["v"][:, h]
+        assert _relerr(pi["num"][:, h] - own, ps["num"][:, h]) < RTOL_EXACT
+        assert _relerr(pi["den"][:, h] - np.sum(pq * pk, axis=1), ps["den"][:, h]) < RTOL_EXACT
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+def test_token_causal_chained_calls_equal_one_call(include_self):
+    grid = (5, 2, 3)
+    inp = _inputs(*grid, 2, 32, 56)
+    o, S, z = _tc(inp, include_self)
+    hw = 6
+    a = {k: (v[: 2 * hw] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+    b = {k: (v[2 * hw:] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+    a["grid"] = (2, 2, 3)
+    b["grid"] = (3, 2, 3)
+    oa, Sa, za = _tc(a, include_self)
+    ob, Sb, zb = _tc(b, include_self, Sa, za, pos_offset=(2, 0, 0))
+    assert _relerr(np.concatenate([oa, ob]), o) < RTOL_EXACT
+    assert _relerr(Sb, S) < RTOL_EXACT and _relerr(zb, z) < RTOL_EXACT
