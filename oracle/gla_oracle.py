@@ -59,6 +59,7 @@ __all__ = [
     "gla_forward",
     "gla_block_causal_forward",
     "gla_token_causal_forward",
+    "gla_token_causal_rows",
     "block_bounds",
 ]
 
@@ -282,3 +283,42 @@ def gla_token_causal_forward(q, k, v, beta, g, rms_w, grid, eps, include_self=Tr
     if not return_parts:
         return out, S_fin, z_fin
     return {"out": out, "S": S_fin, "z": z_fin, "num": nums, "den": dens}
+
+
+def gla_token_causal_rows(q, k, v, beta, g, rms_w, grid, eps, rows, heads=None, include_self=True, S0=None,
+                          z0=None, pos_offset=(0, 0, 0)):
+    """Token-causal output at chosen tokens only, for sequences too long for the
+    dense N x N form (SANA-Video notes, key design 2: the causal form as a
+    running state and key sum).  The running sums are advanced from one chosen
+    token to the next by adding the tokens in between:
+        S(i) = S0 + sum_{j <= i} beta_j v_j rk_j^T,  z(i) = z0 + sum_{j <= i} phi(k_j)
+    and token i reads S(i), z(i) (include_self) or S(i - 1), z(i - 1).
+    Returns out [len(rows), len(heads), d] in the order of `rows`.
+    """
+    T, H, W = grid
+    q = np.asarray(q)
+    d = q.shape[2]
+    head_ids = list(range(q.shape[1])) if heads is None else list(heads)
+    row_ids = np.asarray(rows, dtype=np.int64)
+    order = np.argsort(row_ids, kind="stable")
+    ang = rope_angles(T, H, W, d, pos_offset=pos_offset)
+    w = np.asarray(rms_w, dtype=np.float64)
+    out = np.zeros((len(row_ids), len(head_ids), d))
+    for hi, h in enumerate(head_ids):
+        S = np.zeros((d, d)) if S0 is None else np.asarray(S0[h], dtype=np.float64).copy()
+        z = np.zeros(d) if z0 is None else np.asarray(z0[h], dtype=np.float64).copy()
+        pk, rk = head_features(_head(k, h), ang, eps)
+        vh = _head(v, h)
+        done = 0                     # tokens [0, done) are in (S, z)
+        for m in order:
+            i = int(row_ids[m])
+            upto = i + 1 if include_self else i
+            if upto > done:
+                dS, dz = _state(beta[done:upto, h], vh[done:upto], pk[done:upto], rk[done:upto])
+                S = S + dS
+                z = z + dz
+                done = upto
+            pq, rq = head_features(np.asarray(q[i:i + 1, h, :], dtype=np.float64), ang[i:i + 1], eps)
+            o, _, _, _ = _output_rows(pq, rq, S, z, np.asarray(g[i:i + 1, h, :], dtype=np.float64), w, eps)
+            out[m, hi, :] = o[0]
+    return out

@@ -621,3 +621,22 @@ def test_token_causal_chained_calls_equal_one_call(include_self):
     ob, Sb, zb = _tc(b, include_self, Sa, za, pos_offset=(2, 0, 0))
     assert _relerr(np.concatenate([oa, ob]), o) < RTOL_EXACT
     assert _relerr(Sb, S) < RTOL_EXACT and _relerr(zb, z) < RTOL_EXACT
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+def test_token_causal_rows_match_brute_force(include_self):
+    """The running-sum evaluation at chosen tokens (for long sequences) agrees
+    with the explicit N x N masked brute force, rows given out of order and
+    repeated, with a carried state."""
+    grid = (3, 3, 4)
+    inp = _inputs(*grid, 2, 32, 57)
+    rng = np.random.default_rng(6)
+    S0 = rng.standard_normal((2, 32, 32))
+    z0 = np.abs(rng.standard_normal((2, 32)))
+    rows = np.array([35, 0, 17, 17, 1, 20, 34])
+    got = orc.gla_token_causal_rows(*_args(inp), rows, heads=[1, 0], include_self=include_self, S0=S0, z0=z0,
+                                    pos_offset=(2, 0, 0))
+    bo, _, _ = brute_force(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"].astype(np.float64),
+                           grid, inp["eps"], S0=S0, z0=z0, off=(2, 0, 0),
+                           token_causal="incl" if include_self else "excl")
+    assert _relerr(got, bo[rows][:, [1, 0]]) < RTOL_EXACT
