@@ -1,10 +1,13 @@
 """Benchmark of the gated bidirectional ReLU linear-attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p_60s]
+                    [--form workload|token-causal|token-causal-strict]
 
 One step is one full call of the operator (RoPE tables, state partials,
-reduce, fused output) on one seeded synthetic input set already resident in
-HBM.  Prints ONE JSON line on stdout (progress goes to stderr):
+reduce, fused output or token-causal walk) on one seeded synthetic input set
+already resident in HBM.  The default form is the workload's own
+(bidirectional for 720p_60s); the token-causal forms run the same grid with
+token i reading tokens j <= i (or j < i).  Prints ONE JSON line on stdout (progress goes to stderr):
 tokens/s for the whole step, achieved HBM GB/s of the step's algorithmic
 bytes, the roofline of the dominant kernel (HIP-event durations taken on the
 call's stream during the timed steps), and the fp64 CPU oracle timed on a
@@ -26,7 +29,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
 KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
-                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
+                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip",
+                   "gla_causal.hip")]
 
 
 def log(*a):
@@ -41,10 +45,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def kernel_alg_bytes(w, kernel: str) -> int:
+def kernel_alg_bytes(w, kernel: str, token_causal: bool = False) -> int:
     """Algorithmic HBM bytes one launch of a kernel must move."""
     s = w.elem_size
     big = w.N * w.heads * w.d * s
+    if kernel == "output_kernel" and token_causal:   # read q, k, v, g, beta; write out
+        return 5 * big + w.N * w.heads * s
     if kernel == "output_kernel":        # read q, g; write out
         return 3 * big
     if kernel == "state_partial_kernel":  # read k, v, beta
@@ -105,7 +111,8 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
     w_scale = known_kib / write[ck]
     # every launch of a pass (whichever of its kernel variants ran) is summarised
     # under the timing name of that pass
-    for prefix, short in (("gla::output", "output_kernel"), ("gla::state_partial", "state_partial_kernel")):
+    for prefix, short in (("gla::output", "output_kernel"), ("gla::token_causal", "output_kernel"),
+                          ("gla::state_partial", "state_partial_kernel")):
         names = [k for k in fetch if k.removeprefix("void ").startswith(prefix) and k not in copy]
         if not names:
             continue
@@ -180,6 +187,40 @@ def cpu_baseline(w, inp, heads_sample: int):
     }
 
 
+def cpu_baseline_token_causal(w, inp, include_self: bool, heads_sample: int = 2, target_tokens: int = 1 << 30):
+    """Time the fp64 oracle's running-sum token-causal evaluation on
+    `heads_sample` heads over the first whole frames of the grid (up to
+    target_tokens tokens; every output row) and scale to the whole workload."""
+    import numpy as np
+    import oracle.gla_oracle as orc
+    from workloads import head_slice_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    hw = w.H * w.W
+    frames = max(1, min(w.T, round(target_tokens / hw)))
+    n = frames * hw
+    heads = list(range(min(heads_sample, w.heads)))
+    sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
+        **inp, **{k: inp[k][:, heads] for k in ("q", "k", "v", "g", "beta")}}
+    part = {k: sub[k][:n] for k in ("q", "k", "v", "g", "beta")}
+    t0 = time.perf_counter()
+    orc.gla_token_causal_rows(part["q"], part["k"], part["v"], part["beta"], part["g"], sub["rms_w"],
+                              (frames, w.H, w.W), w.eps, np.arange(n), include_self=include_self)
+    dt = time.perf_counter() - t0
+    scale = (w.N / n) * w.heads / len(heads)
+    return {
+        "value": w.N / (dt * scale),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"token-causal running sums, {len(heads)} of {w.heads} heads, first {frames} of {w.T} frames "
+                  f"({n} tokens, every row), {dt:.2f} s, scaled x{scale:.4g} to the full workload",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +230,9 @@ def main(argv=None):
     ap.add_argument("--dtype", choices=("bf16", "fp8", "f32"), default=None,
                     help="operator I/O dtype (default: the workload's own, bf16 for 720p_60s); "
                          "fp8 = OCP FP8 E4M3 q, k, v, g, beta and out")
+    ap.add_argument("--form", choices=("workload", "token-causal", "token-causal-strict"), default="workload",
+                    help="operator form: the workload's own (bidirectional or block-causal), or the token-level "
+                         "causal form with the own token included (token-causal) or excluded (-strict)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -204,12 +248,14 @@ def main(argv=None):
     ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
     args = ap.parse_args(argv)
 
+    token_causal = args.form != "workload"
+    label = args.workload + ("_token_causal" if token_causal else "")   # names the profiles/ summaries
     if args.stats_summary:
-        write_stats_summary(args.stats_summary, args.workload, args.pmc_commands)
+        write_stats_summary(args.stats_summary, label, args.pmc_commands)
         return 0
     if args.pmc_summary:
         write_traffic_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024,
-                              args.workload, args.pmc_commands)
+                              label, args.pmc_commands)
         return 0
 
     if args.gpus != 1:
@@ -253,12 +299,24 @@ def main(argv=None):
         t["out"] = torch.empty_like(t["q"])
         bufs.append(t)
     rms_w = torch.from_numpy(inp["rms_w"]).to(dev)
+    causal = token_causal or w.block_frames is not None
+    # carried state of the causal forms: each step continues the previous one's
+    state_S = torch.zeros((w.heads, w.d, w.d), dtype=torch.float32, device=dev) if causal else None
+    state_z = torch.zeros((w.heads, w.d), dtype=torch.float32, device=dev) if causal else None
     torch.cuda.synchronize()
-    log(f"[bench] {sets} input set(s) resident on {torch.cuda.get_device_name(dev)}")
+    log(f"[bench] {sets} input set(s) resident on {torch.cuda.get_device_name(dev)}; form {args.form}")
 
     def step(i):
         b = bufs[i % sets]
-        gla.forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, (w.T, w.H, w.W), eps=w.eps, out=b["out"])
+        grid = (w.T, w.H, w.W)
+        if token_causal:
+            gla.token_causal_forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, grid, state_S, state_z,
+                                     include_self=(args.form == "token-causal"), eps=w.eps, out=b["out"])
+        elif w.block_frames is not None:
+            gla.block_causal_forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, grid, state_S, state_z,
+                                     w.block_frames, eps=w.eps, out=b["out"])
+        else:
+            gla.forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, grid, eps=w.eps, out=b["out"])
 
     for i in range(args.warmup):
         step(i)
@@ -277,12 +335,13 @@ def main(argv=None):
 
     ms_step = elapsed * 1e3 / args.steps
     tokens_s = w.N / (ms_step * 1e-3)
-    step_gbps = w.alg_bytes() / (ms_step * 1e-3) / 1e9
+    alg_step = w.alg_bytes() + (2 * w.heads * (w.d * w.d + w.d) * 4 if token_causal else 0)
+    step_gbps = alg_step / (ms_step * 1e-3) / 1e9
     kernels = {k: {"ms_per_launch": (ms / n if n else None), "launches": n} for k, (ms, n) in kt.items()}
     dom = max(("state_partial_kernel", "output_kernel"), key=lambda k: kt[k][0])
     dom_ms = kt[dom][0] / max(1, kt[dom][1])
-    achieved = kernel_alg_bytes(w, dom) / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(dom, w.name) if profiled else None
+    achieved = kernel_alg_bytes(w, dom, token_causal) / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(dom, label) if profiled else None
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
 
@@ -298,7 +357,8 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on {args.cpu_heads} heads ...")
-        cpu = cpu_baseline(w, inp, args.cpu_heads)
+        cpu = (cpu_baseline_token_causal(w, inp, args.form == "token-causal") if token_causal
+               else cpu_baseline(w, inp, args.cpu_heads))
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s ({cpu['sample']})")
 
     rec = {
@@ -321,12 +381,14 @@ def main(argv=None):
             "heads": w.heads,
             "head_dim": w.d,
             "eps": w.eps,
-            "mode": "bidirectional" if w.block_frames is None else f"block-causal F={w.block_frames}",
+            "mode": ({"token-causal": "token-causal (j <= i)", "token-causal-strict": "token-causal (j < i)"}
+                     [args.form] if token_causal else
+                     "bidirectional" if w.block_frames is None else f"block-causal F={w.block_frames}"),
             "input_sets": sets,
         },
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
-        "alg_bytes_per_step": w.alg_bytes(),
+        "alg_bytes_per_step": alg_step,
         "kernels": kernels,
         "roofline": {
             "kernel": dom,

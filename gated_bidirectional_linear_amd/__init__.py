@@ -8,6 +8,8 @@ PyTorch provides device memory and streams.
     out = forward(q, k, v, beta, g, rms_w, (T, H, W), eps=1e-6)
     out = block_causal_forward(q, k, v, beta, g, rms_w, (T, H, W), state_S, state_z,
                                block_frames, eps=1e-6)
+    out = token_causal_forward(q, k, v, beta, g, rms_w, (T, H, W), state_S, state_z,
+                               include_self=True, eps=1e-6)
 
 q, k, v, g: [N, heads, d] (float32, bfloat16 or float8_e4m3fn, contiguous, on the GPU),
 beta: [N, heads] same dtype, rms_w: [d] float32, N = T*H*W, d in {32, 64, 128}.
@@ -21,6 +23,7 @@ from ._lib import LIB_PATH, LibraryNotBuilt, SIGNATURES, load
 __all__ = [
     "forward",
     "block_causal_forward",
+    "token_causal_forward",
     "status_string",
     "version",
     "GlaError",
@@ -140,6 +143,27 @@ def block_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, block_
                                             _ptr(state_S), _ptr(state_z), int(block_frames), int(t_offset), code)
     if st != 0:
         raise GlaError(st, "gla_block_causal_forward_at")
+    return out
+
+
+def token_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, include_self: bool = True,
+                         eps: float = 1e-6, out=None, stream=None, t_offset: int = 0):
+    """Token-level causal operator: token i reads the carried state plus the
+    tokens j <= i (``include_self``) or j < i.  ``state_S`` [heads, d, d] and
+    ``state_z`` [heads, d] (float32) are read and overwritten in place with the
+    state after the last token.  ``t_offset`` is the absolute frame of the
+    call's first frame when a sequence is streamed through successive calls.
+    Returns ``out``."""
+    torch = _torch()
+    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    _check("state_S", state_S, (heads, d, d), torch.float32, q.device)
+    _check("state_z", state_z, (heads, d), torch.float32, q.device)
+    st = load().gla_token_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
+                                         heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
+                                         _ptr(state_S), _ptr(state_z), 1 if include_self else 0, int(t_offset),
+                                         code)
+    if st != 0:
+        raise GlaError(st, "gla_token_causal_forward")
     return out
 
 

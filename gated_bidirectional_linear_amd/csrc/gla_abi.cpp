@@ -37,15 +37,41 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Workgroups aimed for by the token-causal output kernel: one per (head,
+// segment), each walking its segment in order, one per CU at a time.
+constexpr int kDefaultTargetWgTokenCausal = 512;
+constexpr int kTokenTile = 32;   // tokens per step of the token-causal kernel
+
+enum class Form { bidirectional, block_causal, token_causal };
+
+// Segment length: the whole sequence, one block of latent frames, or (token-
+// causal form) a multiple of the 32-token tile chosen for parallelism.
+int segment_length(Form form, int T, int H, int W, int heads, int block_frames) {
+  const long N = (long)T * H * W;
+  if (form == Form::block_causal) {
+    const int frames = (block_frames > 0 && block_frames < T) ? block_frames : T;
+    return frames * H * W;
+  }
+  if (form == Form::token_causal) {
+    const int want = ceil_div(env_int("GLA_TOKEN_CAUSAL_WORKGROUPS", kDefaultTargetWgTokenCausal), heads);
+    const int nseg = want < 1 ? 1 : want;
+    const long len = ((N + nseg - 1) / nseg + kTokenTile - 1) / kTokenTile * kTokenTile;
+    return (int)(len < kTokenTile ? kTokenTile : len);
+  }
+  return (int)N;
+}
+
 // narrow: the I/O dtype is bf16 or fp8, whose rows the fast d = 128 pass-1 kernel takes as bf16
 // words; bf16_io: the I/O dtype is bf16
-Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames, bool narrow, bool bf16_io) {
+Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, bool token_causal, bool narrow,
+              bool bf16_io) {
   Geometry G{};
   G.T = T; G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
   G.N = T * H * W;
-  const int frames = (block_frames > 0 && block_frames < T) ? block_frames : T;
-  G.seg_len = frames * H * W;
+  G.seg_len = seg_len;
   G.nseg = ceil_div(G.N, G.seg_len);
+  G.token_causal = token_causal ? 1 : 0;
+  G.states_exclusive = token_causal ? 1 : 0;
   const int tiles_per_seg = ceil_div(G.seg_len, kTile);
   const int per_seg_heads = heads * G.nseg;
 
@@ -75,7 +101,8 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128.  Its fp8
   // instantiation spills registers at two workgroups per CU and measured slower than the
   // one-head kernel, so fp8 keeps the one-head kernel.
-  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
+  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && env_int("GLA_PASS2_GENERIC", 0) != 1)
+                     ? 1 : 0;
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / 2 : per_seg_heads;
   const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", G.pass2_pair ? kDefaultTargetWgPair2 : kDefaultTargetWg2),
                              per_seg_units2);
@@ -85,6 +112,11 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int block_frames
   G.chunk2 = ceil_div(tiles_per_seg, cps2) * kTile;
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
+  if (token_causal) {   // one workgroup walks a whole segment
+    G.cps2 = 1;
+    G.chunk2 = G.seg_len;
+    G.rope_lds2 = rope_fits(G.seg_len) ? 1 : 0;
+  }
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
   if (!G.rope_lds1) G.pass1_reg = 0;
@@ -199,18 +231,21 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   return GLA_OK;
 }
 
-int run(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w, int T,
-        int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S, float* z,
-        int block_frames, int t_offset) {
-  const bool causal = S != nullptr || z != nullptr || block_frames > 0;
-  const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z, block_frames);
+int run(Form form, const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
+        int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S, float* z,
+        int block_frames, int t_offset, int include_self) {
+  const bool causal = form != Form::bidirectional;
+  const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z,
+                          form == Form::block_causal ? block_frames : 1);
   if (st != GLA_OK) return st;
   const long long N = (long long)T * H * W;
   if (N == 0) return GLA_OK;
 
-  Geometry G = plan(T, H, W, heads, d, eps, causal ? block_frames : 0,
+  const int seg_len = segment_length(form, T, H, W, heads, block_frames);
+  Geometry G = plan(T, H, W, heads, d, eps, seg_len, form == Form::token_causal,
                     dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16);
   G.t_offset = t_offset;
+  G.include_self = include_self;
   const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
@@ -261,7 +296,8 @@ extern "C" {
 
 int gla_forward(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
                 int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype) {
-  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr, nullptr, 0, 0);
+  return run(Form::bidirectional, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr,
+             nullptr, 0, 0, 0);
 }
 
 int gla_block_causal_forward_at(const void* q, const void* k, const void* v, const void* beta, const void* g,
@@ -275,8 +311,22 @@ int gla_block_causal_forward_at(const void* q, const void* k, const void* v, con
     const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
     return st != GLA_OK ? st : GLA_ERR_SHAPE;
   }
-  return run(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S, state_z, block_frames,
-             t_offset);
+  return run(Form::block_causal, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S,
+             state_z, block_frames, t_offset, 0);
+}
+
+int gla_token_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                             const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                             void* stream, float* state_S, float* state_z, int include_self, int t_offset,
+                             int dtype) {
+  const bool args_ok = (include_self == 0 || include_self == 1) && t_offset >= 0 && (long long)t_offset + T <= INT32_MAX;
+  if (!args_ok) {
+    // validate the rest first so dtype/d errors keep their precedence
+    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
+    return st != GLA_OK ? st : GLA_ERR_SHAPE;
+  }
+  return run(Form::token_causal, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S,
+             state_z, 0, t_offset, include_self);
 }
 
 int gla_block_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
@@ -290,7 +340,7 @@ const char* gla_status_string(int status) {
   switch (status) {
     case GLA_OK: return "ok";
     case GLA_ERR_NULL: return "a required pointer is NULL";
-    case GLA_ERR_SHAPE: return "invalid shape, block size, frame offset, eps or size overflow";
+    case GLA_ERR_SHAPE: return "invalid shape, block size, frame offset, causal mode flag, eps or size overflow";
     case GLA_ERR_DTYPE: return "unknown dtype";
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case GLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
@@ -301,7 +351,7 @@ const char* gla_status_string(int status) {
   }
 }
 
-int gla_version(void) { return (1 << 16) | 2; }
+int gla_version(void) { return (1 << 16) | 3; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

@@ -1,0 +1,422 @@
+// Pass 2 of the token-level causal form (SANA-Video notes, key design 2:
+// causal linear attention as running sums of the per-token states and key
+// sums).  Token i of a head reads
+//   S_i = S_seg + sum_{j in seg, j <= i} beta_j v_j (R_j phi k^_j)^T
+//   z_i = z_seg + sum_{j in seg, j <= i} phi k^_j
+// (j < i when the own token is excluded), where (S_seg, z_seg) is the state
+// exclusive of the token's segment that the reduce kernel wrote.
+#include "gla_common.h"
+
+namespace gla {
+
+// One workgroup per (head, segment) walks the segment in 32-token tiles and
+// keeps the running state transposed, S^T (k channel x v channel), in MFMA
+// accumulators: wave w owns v-channel tile w and every k-channel tile.  Per
+// tile, with rq = R phi(q) (raw q; the RMS scale cancels, as in the
+// bidirectional output kernel) and rk = beta R phi(k^):
+//   num^T = S^T-as-A-operand x RQ^T      inter-tile part (state before the tile)
+//         + V^T x AM^T                   intra-tile part, AM_ij = M_ij rk_j . rq_i
+//   S^T  += RK^T x V                     state after the tile
+//   den_i = phi(q_i) . z_i + eps r_i     z_i from an fp32 scan of phi k^ over the tile
+// all on MFMA except the scan.  The accumulator layout of S^T gives lane half
+// h, register r the k channel 8(r/4) + 4h + r%4 of the lane's v column, so the
+// state enters the numerator MFMA straight from registers, with the query
+// operand read in that same channel order.
+template <int D, typename E>
+struct CausalCfg {
+  typedef typename Elem<E>::Lds L;
+  static constexpr int TT = 32;                              // tokens per tile
+  static constexpr int CG = D / 8;                           // 8-channel groups per token
+  static constexpr int TG = kThreads / CG;                   // token groups
+  static constexpr int TPT = TG >= TT ? 1 : TT / TG;         // tokens per thread
+  static constexpr int ACT = TT / TPT;                       // token groups with rows (d = 32 idles the rest)
+  static constexpr int MT = D / 32;                          // 32-channel tiles
+  static constexpr int PADL = Elem<L>::is_bf16 ? 8 : 4;      // elements
+  static constexpr int RP = D + PADL;                        // rqs, rks: [token][channel]
+  static constexpr int CP = TT + PADL;                       // rkT, vT: [channel][token]; am: [i][j]
+  static constexpr int FP = D + 4;                           // zk, nums: [token][channel] fp32
+  static constexpr int RQ_OFF = 0;
+  static constexpr int RK_OFF = RQ_OFF + TT * RP * (int)sizeof(L);
+  static constexpr int RKT_OFF = RK_OFF + TT * RP * (int)sizeof(L);
+  static constexpr int VT_OFF = RKT_OFF + D * CP * (int)sizeof(L);
+  static constexpr int AM_OFF = VT_OFF + D * CP * (int)sizeof(L);
+  static constexpr int ZK_OFF = AM_OFF + TT * CP * (int)sizeof(L);
+  static constexpr int NUM_OFF = ZK_OFF + TT * FP * 4;
+  static constexpr int SMEM = NUM_OFF + TT * FP * 4;
+  static_assert(TPT * ACT == TT && TPT <= 2, "token split");
+  static_assert(kThreads >= D, "scan threads");
+};
+
+// Operand fragments in the channel order of the accumulator layout.
+template <typename L> struct PermFrag;
+template <> struct PermFrag<bf16_t> {
+  static constexpr int STEPS = 2;   // K = 16 steps per 32-channel block
+  // slot j of lane half h in step s is channel 16s + 8(j/4) + 4h + j%4 of the block at p
+  __device__ __forceinline__ static bf16x8 row(const bf16_t* p, int s, int h) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p + 16 * s + 4 * h);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + 16 * s + 8 + 4 * h);
+    return __builtin_bit_cast(bf16x8, (uint4){a.x, a.y, b.x, b.y});
+  }
+  // accumulator registers 8s .. 8s+7 as an operand fragment (rounded to bf16)
+  __device__ __forceinline__ static bf16x8 acc(const f32x16& c, int s) {
+    uint4 u;
+    u.x = pack2bf(c[8 * s + 0], c[8 * s + 1]);
+    u.y = pack2bf(c[8 * s + 2], c[8 * s + 3]);
+    u.z = pack2bf(c[8 * s + 4], c[8 * s + 5]);
+    u.w = pack2bf(c[8 * s + 6], c[8 * s + 7]);
+    return __builtin_bit_cast(bf16x8, u);
+  }
+};
+template <> struct PermFrag<float> {
+  static constexpr int STEPS = 16;  // K = 2 steps per 32-channel block
+  __device__ __forceinline__ static float row(const float* p, int s, int h) { return p[8 * (s >> 2) + 4 * h + (s & 3)]; }
+  __device__ __forceinline__ static float acc(const f32x16& c, int s) { return c[s]; }
+};
+
+// One beta per (token, head) through a buffer resource (rows past it read 0).
+template <typename E> struct BetaLoad;
+template <> struct BetaLoad<float> {
+  typedef uint32_t Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static float value(Raw x) { return __uint_as_float(x); }
+};
+template <> struct BetaLoad<bf16_t> {
+  typedef unsigned short Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static float value(Raw x) { return __uint_as_float((uint32_t)x << 16); }
+};
+template <> struct BetaLoad<fp8_t> {
+  typedef unsigned char Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (unsigned char)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static float value(Raw x) { return __builtin_amdgcn_cvt_f32_fp8((int)x, 0); }
+};
+
+template <int D, typename E, bool LDSR>
+__global__ __launch_bounds__(kThreads) void token_causal_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
+    const E* __restrict__ g, const float* __restrict__ states, const float* __restrict__ rms_w,
+    const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
+  using C = CausalCfg<D, E>;
+  using L = typename C::L;
+  using M = Mfma<L>;
+  using PF = PermFrag<L>;
+  using R = Rope<D>;
+  using BR = BufRow<E>;
+  using BL = BetaLoad<E>;
+  typedef typename BR::Raw Raw;
+  constexpr int TT = C::TT;
+  constexpr int TPT = C::TPT;
+  constexpr int SZ = D * D + D;
+  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
+  L* rqs = reinterpret_cast<L*>(smem + C::RQ_OFF);     // [TT][RP]  rq = R phi(q), raw q
+  L* rks = reinterpret_cast<L*>(smem + C::RK_OFF);     // [TT][RP]  rk = beta R phi(k^)
+  L* rkT = reinterpret_cast<L*>(smem + C::RKT_OFF);    // [D][CP]   rk transposed
+  L* vT = reinterpret_cast<L*>(smem + C::VT_OFF);      // [D][CP]   v transposed
+  L* am = reinterpret_cast<L*>(smem + C::AM_OFF);      // [TT][CP]  masked rk_j . rq_i, row i
+  float* zk = reinterpret_cast<float*>(smem + C::ZK_OFF);    // [TT][FP] phi k^, then its running sums
+  float* nums = reinterpret_cast<float*>(smem + C::NUM_OFF); // [TT][FP] numerators (token, v channel)
+
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  const Chunk ch = chunk_of(lin, G, 1, G.seg_len);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = tid % C::CG;
+  const int tg = tid / C::CG;
+  const bool rows = tg < C::ACT;          // wave-uniform
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const bool incl = G.include_self != 0;
+
+  const uint32_t ROW = (uint32_t)G.heads * D * sizeof(E);
+  const uint32_t head_off = (uint32_t)ch.head * D * sizeof(E);
+  const uint32_t BROW = (uint32_t)G.heads * sizeof(E);
+  const uint32_t bhead_off = (uint32_t)ch.head * sizeof(E);
+  // rows [t0, min(t0 + TT, segment end)) of this head: past them loads read 0
+  // and stores are dropped
+  auto tile_rows = [&](long t0) -> uint32_t {
+    const long left = ch.end - t0;
+    return left <= 0 ? 0u : (left >= TT ? (uint32_t)TT : (uint32_t)left);
+  };
+  auto tile_rsrc = [&](const void* p, long t0) {
+    const uint32_t n = tile_rows(t0);
+    return make_rsrc(reinterpret_cast<const char*>(p) + (size_t)t0 * ROW + head_off, n == 0 ? 0u : n * ROW - head_off);
+  };
+  auto beta_rsrc = [&](long t0) {
+    const uint32_t n = tile_rows(t0);
+    return make_rsrc(reinterpret_cast<const char*>(beta) + (size_t)t0 * BROW + bhead_off,
+                     n == 0 ? 0u : n * BROW - bhead_off);
+  };
+  uint32_t voff[TPT], boff[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    voff[i] = (uint32_t)(tg * TPT + i) * ROW + 8u * cg * sizeof(E);
+    boff[i] = (uint32_t)(tg * TPT + i) * BROW;
+  }
+
+  // running state: S^T tiles of this wave's v columns, and (scan threads) z
+  const float* Sst = states + ((size_t)ch.seg * G.heads + ch.head) * SZ;
+  f32x16 st[C::MT];
+  if (wave < C::MT) {
+#pragma unroll
+    for (int ct = 0; ct < C::MT; ++ct)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sst + (size_t)(32 * wave + l32) * D + 32 * ct + 8 * rb + 4 * hi);
+        st[ct][4 * rb] = s4.x; st[ct][4 * rb + 1] = s4.y; st[ct][4 * rb + 2] = s4.z; st[ct][4 * rb + 3] = s4.w;
+      }
+  }
+  const int zc = tid - (kThreads - D);     // scan thread's channel
+  float zrun = zc >= 0 ? Sst[D * D + zc] : 0.f;
+  float wc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) wc[c] = rms_w[8 * cg + c];
+
+  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  GridPos pos;
+  pos.set((int)min(ch.begin + (long)tg * TPT, (long)G.N - 1), G.H, G.W);
+  const int HW = G.H * G.W;
+  const int adt = TT / HW, ady = (TT % HW) / G.W, adx = TT % G.W;
+
+  Raw qr[TPT], kr[TPT], vr[TPT], gr[TPT];
+  typename BL::Raw br[TPT];
+  auto issue_qkvb = [&](long t0) {
+    const __amdgpu_buffer_rsrc_t qs = tile_rsrc(q, t0), ks = tile_rsrc(k, t0), vs = tile_rsrc(v, t0);
+    const __amdgpu_buffer_rsrc_t bs = beta_rsrc(t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      qr[i] = BR::load(qs, voff[i], 0);
+      kr[i] = BR::load(ks, voff[i], 0);
+      vr[i] = BR::load(vs, voff[i], 0);
+      br[i] = BL::load(bs, boff[i]);
+    }
+  };
+  auto issue_g = [&](long t0) {
+    const __amdgpu_buffer_rsrc_t gs = tile_rsrc(g, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) gr[i] = BR::load(gs, voff[i], 0);
+  };
+  issue_qkvb(ch.begin);
+  issue_g(ch.begin);
+  if constexpr (LDSR) lds_barrier();
+
+  for (long t0 = ch.begin; t0 < ch.end; t0 += TT) {
+    // ---- A: token features (row layout), this tile's rows -> LDS ----------
+    float phq[TPT][8], rq_scale[TPT];
+    if (rows) {
+      typename R::CS cs[TPT];
+      GridPos pp = pos;
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        // rows past the segment end (zero k, v, beta; outputs dropped) take the
+        // last staged frame's angles so that every factor stays finite
+        cs[i] = R::fetch(rv, cg, min(pp.t, rv.t_lo + rv.nt - 1), pp.y, pp.x);
+        pp.next(G.H, G.W);
+      }
+      float kx[TPT][8], vx[TPT][8];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int tok = tg * TPT + i;
+        float qx[8];
+        Elem<E>::unpack(qr[i], qx);
+        Elem<E>::unpack(kr[i], kx[i]);
+        Elem<E>::unpack(vr[i], vx[i]);
+        const float bt = BL::value(br[i]);
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          ssq += qx[c] * qx[c];
+          ssk += kx[i][c] * kx[i][c];
+        }
+        ssq = group_sum<C::CG>(ssq);
+        ssk = group_sum<C::CG>(ssk);
+        const float msq = ssq * (1.0f / D) + G.eps;
+        rq_scale[i] = msq * __builtin_amdgcn_rsqf(msq);      // r = sqrt(mean(q^2) + eps)
+        const float inv = rsqrtf(ssk * (1.0f / D) + G.eps);
+        float rq[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          phq[i][c] = fmaxf(qx[c], 0.f);
+          rq[c] = phq[i][c];
+          kx[i][c] = fmaxf(kx[i][c] * inv, 0.f);           // phi(k^)
+        }
+        float* zrow = zk + tok * C::FP + 8 * cg;
+        *reinterpret_cast<f32x4*>(zrow) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
+        *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
+        R::apply(rq, cs[i]);
+        R::apply(kx[i], cs[i]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) kx[i][c] *= bt;             // rk
+        L* qd = rqs + tok * C::RP + 8 * cg;
+        L* kd = rks + tok * C::RP + 8 * cg;
+        if constexpr (Elem<L>::is_bf16) {
+          *reinterpret_cast<u32x4*>(qd) = Elem<bf16_t>::pack(rq);
+          *reinterpret_cast<u32x4*>(kd) = Elem<bf16_t>::pack(kx[i]);
+        } else {
+          *reinterpret_cast<f32x4*>(qd) = (f32x4){rq[0], rq[1], rq[2], rq[3]};
+          *reinterpret_cast<f32x4*>(qd + 4) = (f32x4){rq[4], rq[5], rq[6], rq[7]};
+          *reinterpret_cast<f32x4*>(kd) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
+          *reinterpret_cast<f32x4*>(kd + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        store_tcol<L, TPT>(rkT + (8 * cg + c) * C::CP + tg * TPT, kx, c);
+        store_tcol<L, TPT>(vT + (8 * cg + c) * C::CP + tg * TPT, vx, c);
+      }
+    }
+    pos.advance(adt, ady, adx, G.H, G.W);
+    issue_qkvb(t0 + TT);   // the next tile's q, k, v, beta rows (zero past the segment)
+    lds_barrier();
+
+    // ---- B: masked intra-tile scores, key-sum scan, state update ------------
+    if (wave == 0) {
+      // AM^T[j][i] = rk_j . rq_i on MFMA (A = RK rows, B = RQ rows), masked, stored as am[i][j]
+      f32x16 a = {};
+#pragma unroll
+      for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+        const typename M::frag fa = M::lds_frag(rks + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
+        const typename M::frag fb = M::lds_frag(rqs + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
+        a = M::mma(fa, fb, a);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int j0 = 8 * rb + 4 * hi;
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          const bool keep = incl ? j <= l32 : j < l32;
+          x[r] = keep ? a[4 * rb + r] : 0.f;
+        }
+        L* dst = am + l32 * C::CP + j0;
+        if constexpr (Elem<L>::is_bf16)
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack2bf(x[0], x[1]), pack2bf(x[2], x[3]));
+        else
+          *reinterpret_cast<f32x4*>(dst) = (f32x4){x[0], x[1], x[2], x[3]};
+      }
+    }
+    if (zc >= 0) {
+      // running key sums z_i of this tile's tokens (inclusive or exclusive of token i)
+      float x[TT];
+#pragma unroll
+      for (int j = 0; j < TT; ++j) x[j] = zk[j * C::FP + zc];
+#pragma unroll
+      for (int j = 0; j < TT; ++j) {
+        const float nxt = zrun + x[j];
+        zk[j * C::FP + zc] = incl ? nxt : zrun;
+        zrun = nxt;
+      }
+    }
+    typename M::frag sa[C::MT][PF::STEPS];
+    typename M::frag vb[TT / M::KSTEP];
+    if (wave < C::MT) {
+#pragma unroll
+      for (int ct = 0; ct < C::MT; ++ct)
+#pragma unroll
+        for (int s = 0; s < PF::STEPS; ++s) sa[ct][s] = PF::acc(st[ct], s);
+      // S^T += RK^T V: A = rkT[c][j], B = vT[v][j] (v column of this wave)
+#pragma unroll
+      for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
+        vb[ks] = M::lds_frag(vT + (32 * wave + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
+#pragma unroll
+        for (int ct = 0; ct < C::MT; ++ct) {
+          const typename M::frag fa = M::lds_frag(rkT + (32 * ct + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
+          st[ct] = M::mma(fa, vb[ks], st[ct]);
+        }
+      }
+    }
+    lds_barrier();
+
+    // ---- C: numerators on MFMA, denominators from the scanned key sums -------
+    if (wave < C::MT) {
+      f32x16 n = {};
+#pragma unroll
+      for (int ct = 0; ct < C::MT; ++ct)
+#pragma unroll
+        for (int s = 0; s < PF::STEPS; ++s) n = M::mma(sa[ct][s], PF::row(rqs + l32 * C::RP + 32 * ct, s, hi), n);
+#pragma unroll
+      for (int ks = 0; ks < TT / M::KSTEP; ++ks)
+        n = M::mma(vb[ks], M::lds_frag(am + l32 * C::CP + ks * M::KSTEP + M::KPL * hi), n);
+      float* row = nums + l32 * C::FP + 32 * wave + 4 * hi;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<f32x4*>(row + 8 * rb) = (f32x4){n[4 * rb], n[4 * rb + 1], n[4 * rb + 2], n[4 * rb + 3]};
+    }
+    float rden[TPT];
+    if (rows) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const float* zrow = zk + (tg * TPT + i) * C::FP + 8 * cg;
+        const f32x4 za = *reinterpret_cast<const f32x4*>(zrow);
+        const f32x4 zb = *reinterpret_cast<const f32x4*>(zrow + 4);
+        float dp = phq[i][0] * za.x + phq[i][1] * za.y + phq[i][2] * za.z + phq[i][3] * za.w +
+                   phq[i][4] * zb.x + phq[i][5] * zb.y + phq[i][6] * zb.z + phq[i][7] * zb.w;
+        dp = group_sum<C::CG>(dp);
+        rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * rq_scale[i]);
+      }
+    }
+    lds_barrier();
+
+    // ---- D: gate, RMSNorm, store --------------------------------------------
+    if (rows) {
+      const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const float* src = nums + (tg * TPT + i) * C::FP + 8 * cg;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+        float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float gv[8];
+        Elem<E>::unpack(gr[i], gv);
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));
+          ss += y[c] * y[c];
+        }
+        ss = group_sum<C::CG>(ss);
+        const float rd = rden[i];
+        const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
+        BR::store(ors, voff[i], 0, Elem<E>::pack(y));
+      }
+    }
+    issue_g(t0 + TT);
+  }
+}
+
+template <int D, typename E>
+hipError_t launch_token_causal(const LaunchArgs& a) {
+  const Geometry& G = a.geo;
+  const int blocks = G.heads * G.nseg;
+  if (G.rope_lds2)
+    hipLaunchKernelGGL((token_causal_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.q,
+                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g, (const float*)a.states,
+                       a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+  else
+    hipLaunchKernelGGL((token_causal_kernel<D, E, false>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.q,
+                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g, (const float*)a.states,
+                       a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+  return hipGetLastError();
+}
+
+template hipError_t launch_token_causal<32, float>(const LaunchArgs&);
+template hipError_t launch_token_causal<64, float>(const LaunchArgs&);
+template hipError_t launch_token_causal<128, float>(const LaunchArgs&);
+template hipError_t launch_token_causal<32, bf16_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<64, bf16_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<128, bf16_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<32, fp8_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<64, fp8_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<128, fp8_t>(const LaunchArgs&);
+
+}  // namespace gla

@@ -59,6 +59,31 @@ __device__ __forceinline__ void unpack_rows(const typename Elem<E>::Raw (&r)[TPT
   }
 }
 
+// Write TPT consecutive-token values of one channel into a transposed LDS row.
+template <typename E, int TPT>
+__device__ __forceinline__ void store_tcol(E* dst, const float (&x)[TPT][8], int c) {
+  if constexpr (Elem<E>::is_bf16) {
+    if constexpr (TPT == 4) {
+      uint2 u;
+      u.x = pack2bf(x[0][c], x[1][c]);
+      u.y = pack2bf(x[2][c], x[3][c]);
+      *reinterpret_cast<uint2*>(dst) = u;
+    } else if constexpr (TPT == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack2bf(x[0][c], x[1][c]);
+    } else {
+      *dst = f2bf(x[0][c]);
+    }
+  } else {
+    if constexpr (TPT == 4) {
+      *reinterpret_cast<float4*>(dst) = make_float4(x[0][c], x[1][c], x[2][c], x[3][c]);
+    } else if constexpr (TPT == 2) {
+      *reinterpret_cast<float2*>(dst) = make_float2(x[0][c], x[1][c]);
+    } else {
+      *dst = x[0][c];
+    }
+  }
+}
+
 // Stage the RoPE rows of the frames a chunk spans (or use the global table).
 template <int D, bool LDSR>
 __device__ __forceinline__ typename Rope<D>::View rope_view(float2* lds, const float2* __restrict__ rope,

@@ -1,5 +1,6 @@
 // Launch sequence of one operator call: RoPE table, state partials,
-// reduce/prefix, fused output, each bracketed by the optional timer.
+// reduce/prefix, fused output (or the token-causal walk), each bracketed by
+// the optional timer.
 #include "gla_launch.h"
 
 namespace gla {
@@ -11,6 +12,7 @@ template <int D> hipError_t launch_rope_table(const LaunchArgs& a);
 template <int D> hipError_t launch_state_reduce(const LaunchArgs& a);
 template <int D, typename E> hipError_t launch_state_partial(const LaunchArgs& a);
 template <int D, typename E> hipError_t launch_output(const LaunchArgs& a);
+template <int D, typename E> hipError_t launch_token_causal(const LaunchArgs& a);
 
 template <int D, typename E>
 static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
@@ -28,7 +30,7 @@ static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
   tm.end(2, a.stream);
   if (e != hipSuccess) return e;
   tm.begin(3, a.stream);
-  e = launch_output<D, E>(a);
+  e = a.geo.token_causal ? launch_token_causal<D, E>(a) : launch_output<D, E>(a);
   tm.end(3, a.stream);
   return e;
 }

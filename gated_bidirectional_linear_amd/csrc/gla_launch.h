@@ -47,6 +47,9 @@ struct Geometry {
   int pass1_reg;  // pass 1 uses the register-accumulating kernel (bf16, d = 128, RoPE rows in LDS)
   int pass2_pair; // pass 2 takes heads in pairs (bf16, d = 128, even heads, RoPE rows in LDS)
   int t_offset;   // absolute frame of the call's frame 0 (RoPE positions only)
+  int token_causal;   // token-level causal form: segments of seg_len tokens walked in order
+  int include_self;   // token-causal: token i reads tokens j <= i (1) or j < i (0)
+  int states_exclusive;  // per-segment states exclude their own segment (token-causal)
   float eps;
 };
 

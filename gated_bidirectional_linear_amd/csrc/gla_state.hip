@@ -25,31 +25,6 @@ struct PartialCfg {
                                                        : (ZRED_BYTES > KRED_BYTES ? ZRED_BYTES : KRED_BYTES);
 };
 
-// Write TPT consecutive-token values of one channel into a transposed LDS row.
-template <typename E, int TPT>
-__device__ __forceinline__ void store_tcol(E* dst, const float (&x)[TPT][8], int c) {
-  if constexpr (Elem<E>::is_bf16) {
-    if constexpr (TPT == 4) {
-      uint2 u;
-      u.x = pack2bf(x[0][c], x[1][c]);
-      u.y = pack2bf(x[2][c], x[3][c]);
-      *reinterpret_cast<uint2*>(dst) = u;
-    } else if constexpr (TPT == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = pack2bf(x[0][c], x[1][c]);
-    } else {
-      *dst = f2bf(x[0][c]);
-    }
-  } else {
-    if constexpr (TPT == 4) {
-      *reinterpret_cast<float4*>(dst) = make_float4(x[0][c], x[1][c], x[2][c], x[3][c]);
-    } else if constexpr (TPT == 2) {
-      *reinterpret_cast<float2*>(dst) = make_float2(x[0][c], x[1][c]);
-    } else {
-      *dst = x[0][c];
-    }
-  }
-}
-
 template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,

@@ -32,7 +32,9 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 
 // ===========================================================================
 // 3. Reduce chunk partials per segment (pairwise tree of fixed shape), then
-//    inclusive prefix over segments on top of the carried state.
+//    prefix over segments on top of the carried state: inclusive of the
+//    segment (bidirectional and block-causal forms) or exclusive (the
+//    token-causal form, whose segments are walked token by token).
 // ===========================================================================
 template <int D>
 __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restrict__ partial,
@@ -54,8 +56,9 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
     for (int w = kMaxChunks / 2; w >= 1; w >>= 1)
 #pragma unroll
       for (int i = 0; i < w; ++i) v[i] += v[i + w];
+    if (G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
     running += v[0];
-    states[((size_t)s * G.heads + h) * SZ + e] = running;
+    if (!G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
   }
   if (S_out != nullptr) {
     if (e < D * D) S_out[(size_t)h * D * D + e] = running;

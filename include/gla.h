@@ -16,7 +16,8 @@
  * The block-causal form (SANA-Video notes, key design 2: cumulative state and
  * key sum as a constant-memory cache) visits blocks of `block_frames` latent
  * frames in order; tokens of block b read S and z summed over blocks <= b plus
- * the carried state passed in.
+ * the carried state passed in.  The token-causal form (same passage: running
+ * sums per token) has token i read the sums over the tokens up to i.
  *
  * Conventions (the pages leave them open; one reading is fixed here):
  *   - token n = (t*H + y)*W + x, w fastest;
@@ -49,7 +50,8 @@ extern "C" {
 typedef enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL */
-  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, bad t_offset, eps not finite or below FLT_MIN, size overflow */
+  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, bad t_offset or include_self,
+                                 eps not finite or below FLT_MIN, size overflow */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
   GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
@@ -127,6 +129,37 @@ int gla_block_causal_forward_at(const void* q, const void* k, const void* v, con
                                 const void* g, const float* rms_w, int T, int H, int W, int heads,
                                 int d, float eps, void* out, void* stream, float* state_S,
                                 float* state_z, int block_frames, int t_offset, int dtype);
+
+/*
+ * Token-level causal operator (SANA-Video notes, key design 2: causal linear
+ * attention written as running sums over the tokens up to the current one of
+ * the per-token states and key sums).  Tokens are taken in the order
+ * n = (t*H + y)*W + x.  Token i reads
+ *     S_i = S_0 + sum_{j in J(i)} beta_j v_j (R_j phi(k^_j))^T
+ *     z_i = z_0 + sum_{j in J(i)} phi(k^_j)
+ * with J(i) = {j <= i} when include_self is 1 and {j < i} (strictly earlier
+ * tokens, the notes' sums up to i - 1) when it is 0, and
+ *     x_i = sigmoid(g_i) * (S_i R_i phi(q^_i)) / (phi(q^_i) . z_i + eps),
+ *     out_i = rms_w * x_i / sqrt(mean(x_i^2) + eps).
+ *
+ * Same tensors as gla_forward, plus
+ *   state_S, state_z : the carried state (S_0, z_0) as in
+ *                      gla_block_causal_forward: read on entry, overwritten
+ *                      with the state after the last token (which includes
+ *                      every token of the call, whatever include_self is).
+ *   include_self     : 0 or 1, as above.
+ *   t_offset         : absolute latent frame of this call's frame 0, >= 0,
+ *                      t_offset + T <= INT32_MAX.  Calling with frames [0, T1)
+ *                      and then, on the returned state, with frames [T1, T)
+ *                      and t_offset = T1 gives the output and state of one
+ *                      call over [0, T).
+ * A bad include_self or t_offset returns GLA_ERR_SHAPE.  When N == 0 the state
+ * is left unchanged.
+ */
+int gla_token_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                             const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                             void* stream, float* state_S, float* state_z, int include_self, int t_offset,
+                             int dtype);
 
 /* Static text for a gla_status value (never NULL). */
 const char* gla_status_string(int status);

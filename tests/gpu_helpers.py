@@ -95,3 +95,18 @@ def run_block_causal(dev: dict, grid, eps, block_frames, S0=None, z0=None, t_off
                                    S, z, block_frames, eps=eps, t_offset=t_offset)
     torch.cuda.synchronize()
     return out, S, z
+
+
+def run_token_causal(dev: dict, grid, eps, include_self=True, S0=None, z0=None, t_offset=0):
+    import gated_bidirectional_linear_amd as gla
+    torch = torch_mod()
+    N, heads, d = dev["q"].shape
+    S = torch.zeros((heads, d, d), dtype=torch.float32, device=dev["q"].device)
+    z = torch.zeros((heads, d), dtype=torch.float32, device=dev["q"].device)
+    if S0 is not None:
+        S.copy_(torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)))
+        z.copy_(torch.from_numpy(np.ascontiguousarray(z0, dtype=np.float32)))
+    out = gla.token_causal_forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], grid,
+                                   S, z, include_self=include_self, eps=eps, t_offset=t_offset)
+    torch.cuda.synchronize()
+    return out, S, z

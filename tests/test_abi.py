@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
-    assert lib.gla_version() & 0xFFFF >= 2          # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O
+    assert lib.gla_version() & 0xFFFF >= 3   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
@@ -68,6 +68,32 @@ def bc_at(lib, F=1, t_offset=0, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1,
     p = list(P if ptrs is None else ptrs)
     return lib.gla_block_causal_forward_at(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None,
                                            p[7], p[8], F, t_offset, dtype)
+
+
+def tc(lib, include_self=1, t_offset=0, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_token_causal_forward(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None,
+                                        p[7], p[8], include_self, t_offset, dtype)
+
+
+def test_token_causal_argument_errors(lib):
+    assert tc(lib, include_self=2) == E_SHAPE
+    assert tc(lib, include_self=-1) == E_SHAPE
+    assert tc(lib, t_offset=-1) == E_SHAPE
+    assert tc(lib, t_offset=2**31 - 2, T=5) == E_SHAPE
+    assert tc(lib, include_self=2, dtype=7) == E_DTYPE     # dtype keeps its precedence
+    assert tc(lib, d=48) == E_D
+    assert tc(lib, heads=0) == E_SHAPE
+    for i in (0, 6, 7, 8):
+        p = list(P)
+        p[i] = None
+        assert tc(lib, ptrs=p) == E_NULL, i
+    p = list(P)
+    p[7] = p[6]          # state_S over out
+    assert tc(lib, ptrs=p) == E_ALIAS
+    nulls = [None] * 10
+    assert tc(lib, T=0, ptrs=nulls) == OK                   # empty grid
+    assert tc(lib, include_self=0, t_offset=7, T=0, ptrs=nulls) == OK
 
 
 def test_frame_offset_errors(lib):

@@ -1,0 +1,182 @@
+"""GPU parity of the token-level causal form: the HIP path (through the C ABI)
+against the fp64 oracle, element by element on seeded inputs, for both
+readings of whether a token reads its own contribution.
+
+Tolerances as for the other forms: max|err| <= 1e-5 * max|ref| for fp32,
+<= 2e-2 * max|ref| for bf16 (fp8: beyond the output's own rounding).
+"""
+import numpy as np
+import pytest
+
+import oracle.gla_oracle as orc
+from workloads import WORKLOADS, make_inputs, make_workload_inputs, make_state, head_slice_f32
+from tests.gpu_helpers import TOL, Z_TOL, to_device, to_f64, rel_err, fp8_excess, run_token_causal
+
+pytestmark = pytest.mark.gpu
+
+S_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+
+
+def _oracle_tc(inp, include_self, S0=None, z0=None, **kw):
+    return orc.gla_token_causal_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["rms_w"],
+                                        inp["grid"], inp["eps"], include_self=include_self, S0=S0, z0=z0, **kw)
+
+
+def _out_err(got, ref, dtype):
+    return fp8_excess(got, ref) if dtype == "fp8" else rel_err(got, ref)
+
+
+def _check(name, inp, include_self, S0=None, z0=None, t_offset=0):
+    dtype = inp["dtype"]
+    out, S, z = run_token_causal(to_device(inp), inp["grid"], inp["eps"], include_self, S0, z0, t_offset)
+    ro, rS, rz = _oracle_tc(inp, include_self, S0, z0, pos_offset=(t_offset, 0, 0))
+    o = to_f64(out)
+    err = _out_err(o, ro, dtype)
+    print(f"[parity] {name}: rel err {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
+    assert np.all(np.isfinite(o))
+    assert err <= TOL[dtype]
+    assert rel_err(to_f64(S), rS) <= S_TOL[dtype]
+    assert rel_err(to_f64(z), rz) <= Z_TOL[dtype]
+    return o
+
+
+# (T, H, W, heads, d, dtype); N spans several 32-token tiles with a ragged tail
+SHAPES = [
+    (2, 4, 4, 2, 32, "f32"),     # the tiny configuration
+    (3, 5, 7, 3, 64, "f32"),
+    (2, 3, 5, 2, 128, "f32"),
+    (3, 5, 7, 3, 64, "bf16"),
+    (4, 6, 10, 4, 128, "bf16"),
+    (3, 5, 7, 2, 32, "bf16"),
+    (3, 4, 5, 2, 128, "fp8"),
+    (2, 5, 9, 2, 64, "fp8"),
+]
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_token_causal_shapes(shape, include_self):
+    T, H, W, heads, d, dtype = shape
+    print(f"[case] token-causal {shape} include_self={include_self}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=31)
+    _check(f"tc {shape} incl={include_self}", inp, include_self)
+
+
+@pytest.mark.parametrize("wg", ["1", "3", "64"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_causal_segment_counts(monkeypatch, wg, dtype):
+    """One segment walked by one workgroup per head, a few segments of many
+    tiles, or many one-tile segments: the same result."""
+    T, H, W, heads, d = 5, 7, 9, 2, 128
+    monkeypatch.setenv("GLA_TOKEN_CAUSAL_WORKGROUPS", str(int(wg) * heads))
+    print(f"[case] token-causal segments={wg} {dtype}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=32)
+    _check(f"tc segments {wg} {dtype}", inp, True)
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_causal_carried_state(dtype, include_self):
+    T, H, W, heads, d = 3, 6, 8, 2, 128
+    print(f"[case] token-causal carried state {dtype} include_self={include_self}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=33)
+    S0, z0 = make_state(heads, d, seed=4, scale=3.0)
+    _check(f"tc carried state {dtype} incl={include_self}", inp, include_self, S0, z0)
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_causal_chained_calls(dtype, include_self):
+    """A sequence streamed through calls on frame ranges, with frame offsets,
+    gives the output and final state of one call (and of the oracle)."""
+    T, H, W, heads, d = 7, 5, 6, 2, 64
+    hw = H * W
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=34)
+    one = _check(f"tc one call {dtype}", inp, include_self)
+    S, z = None, None
+    outs = []
+    for t0, t1 in ((0, 2), (2, 3), (3, 7)):
+        part = {k: (v[t0 * hw: t1 * hw] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+        part["grid"] = (t1 - t0, H, W)
+        o, S_t, z_t = run_token_causal(to_device(part), part["grid"], part["eps"], include_self, S, z, t_offset=t0)
+        outs.append(to_f64(o))
+        S, z = S_t.cpu().numpy(), z_t.cpu().numpy()
+    chained = np.concatenate(outs)
+    ro, rS, rz = _oracle_tc(inp, include_self)
+    err = rel_err(chained, ro)
+    print(f"[parity] tc chained {dtype} incl={include_self}: rel err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    assert rel_err(chained, one) <= (1e-5 if dtype == "f32" else 1e-2)
+    assert rel_err(S.astype(np.float64), rS) <= S_TOL[dtype]
+    assert rel_err(z.astype(np.float64), rz) <= Z_TOL[dtype]
+
+
+def test_token_causal_first_token_strict_is_zero():
+    """Strictly earlier tokens and no carried state: token 0 reads nothing and
+    its output is exactly zero."""
+    inp = make_inputs(2, 4, 4, 2, 64, "bf16", seed=35)
+    out, _, _ = run_token_causal(to_device(inp), inp["grid"], inp["eps"], False)
+    o = to_f64(out)
+    assert np.all(o[0] == 0.0)
+    assert np.all(np.isfinite(o))
+
+
+def test_token_causal_global_rope_table(monkeypatch):
+    monkeypatch.setenv("GLA_ROPE_GLOBAL", "1")
+    inp = make_inputs(4, 6, 7, 2, 128, "bf16", seed=36)
+    _check("tc global rope", inp, True)
+
+
+def test_token_causal_deterministic():
+    torch = pytest.importorskip("torch")
+    inp = make_inputs(3, 8, 9, 4, 128, "bf16", seed=37)
+    dev = to_device(inp)
+    a, Sa, za = run_token_causal(dev, inp["grid"], inp["eps"], True)
+    b, Sb, zb = run_token_causal(dev, inp["grid"], inp["eps"], True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(Sa, Sb) and torch.equal(za, zb)
+
+
+def test_token_causal_empty_grid_leaves_state():
+    torch = pytest.importorskip("torch")
+    import gated_bidirectional_linear_amd as gla
+    q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    beta = torch.zeros((0, 2), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(64, device="cuda")
+    S = torch.full((2, 64, 64), 1.5, device="cuda")
+    z = torch.full((2, 64), 0.5, device="cuda")
+    gla.token_causal_forward(q, q, q, beta, q, w, (0, 4, 4), S, z)
+    torch.cuda.synchronize()
+    assert bool((S == 1.5).all()) and bool((z == 0.5).all())
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+def test_token_causal_long_sequence_sampled(include_self):
+    """720p/60s (N = 159,280, 32 heads) at full size in the default launch
+    plan: the oracle evaluates 4 heads at sampled tokens (segment boundaries
+    included) by running sums, and the final state of those heads."""
+    torch = pytest.importorskip("torch")
+    w = WORKLOADS["720p_60s"]
+    print(f"[case] token-causal {w.name} N={w.N} heads={w.heads} include_self={include_self}", flush=True)
+    inp = make_workload_inputs(w, seed=0, keep_f32=False)
+    dev = to_device(inp)
+    out, S, z = run_token_causal(dev, inp["grid"], inp["eps"], include_self)
+    o32 = out.float()
+    assert bool(torch.isfinite(o32).all())
+    # default plan: 512 workgroups -> 16 segments of 9,984 tokens per head
+    seg = 9984
+    bounds = [s * seg + dlt for s in range(1, 16) for dlt in (-1, 0, 1)]
+    rng = np.random.default_rng(321)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, w.N - 1], bounds, rng.integers(0, w.N, 200)]))
+    heads = [0, 13, 31]
+    sub = head_slice_f32(inp, heads)
+    ref = orc.gla_token_causal_rows(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"],
+                                    sub["eps"], rows, include_self=include_self)
+    got = to_f64(out[torch.from_numpy(rows).cuda()][:, heads, :])
+    err = rel_err(got, ref)
+    print(f"[parity] tc 720p_60s sampled incl={include_self}: rel err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    parts = orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"],
+                            sub["eps"], rows=np.array([0]), return_parts=True)
+    assert rel_err(to_f64(S[heads]), parts["S"]) <= S_TOL["bf16"]
+    assert rel_err(to_f64(z[heads]), parts["z"]) <= Z_TOL["bf16"]
