@@ -29,17 +29,18 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
 KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
-                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip",
-                   "gla_causal.hip")]
+                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
+CAUSAL_SOURCES = KERNEL_SOURCES + ["gated_bidirectional_linear_amd/csrc/gla_causal.hip"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(token_causal: bool = False) -> str:
+    """Hash of the kernel sources a form's launches are built from."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (CAUSAL_SOURCES if token_causal else KERNEL_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -58,7 +59,7 @@ def kernel_alg_bytes(w, kernel: str, token_causal: bool = False) -> int:
     return 0
 
 
-def read_traffic(kernel: str, workload: str):
+def read_traffic(kernel: str, workload: str, token_causal: bool = False):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a copy-kernel calibration), stored under profiles/.
     None when absent or taken on different kernel sources."""
@@ -71,7 +72,7 @@ def read_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(token_causal):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -94,7 +95,8 @@ def _pmc_means(csv_path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in sums.items()}
 
 
-def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, commands: str) -> None:
+def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, commands: str,
+                          token_causal: bool = False) -> None:
     """Turn FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into HBM bytes per
     launch of the two streaming kernels, each counter scaled by what it reads
     for a device-to-device copy of calib_mib MiB (read calib_mib, write calib_mib)."""
@@ -135,11 +137,11 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
             f.write(f"read_bytes_per_launch: {fetched:.0f}\n")
             f.write(f"write_bytes_per_launch: {written:.0f}\n")
             f.write(f"traffic_bytes_per_launch: {fetched + written:.0f}\n")
-            f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+            f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
         print(f"wrote {path}: {(fetched + written) / 1e9:.3f} GB per launch")
 
 
-def write_stats_summary(stats_csv: str, workload: str, commands: str) -> None:
+def write_stats_summary(stats_csv: str, workload: str, commands: str, token_causal: bool = False) -> None:
     """Kernel-trace statistics (rocprofv3 --kernel-trace --stats, kernel_stats.csv)
     as a short text table under profiles/."""
     import csv
@@ -155,7 +157,7 @@ def write_stats_summary(stats_csv: str, workload: str, commands: str) -> None:
             name = r["Name"].split("(")[0].replace("void ", "")
             f.write(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}\n")
-        f.write(f"kernel_source_sha256: {kernel_source_hash()}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
     print(f"wrote {path}")
 
 
@@ -251,11 +253,11 @@ def main(argv=None):
     token_causal = args.form != "workload"
     label = args.workload + ("_token_causal" if token_causal else "")   # names the profiles/ summaries
     if args.stats_summary:
-        write_stats_summary(args.stats_summary, label, args.pmc_commands)
+        write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal)
         return 0
     if args.pmc_summary:
         write_traffic_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024,
-                              label, args.pmc_commands)
+                              label, args.pmc_commands, token_causal)
         return 0
 
     if args.gpus != 1:
@@ -341,7 +343,7 @@ def main(argv=None):
     dom = max(("state_partial_kernel", "output_kernel"), key=lambda k: kt[k][0])
     dom_ms = kt[dom][0] / max(1, kt[dom][1])
     achieved = kernel_alg_bytes(w, dom, token_causal) / (dom_ms * 1e-3) / 1e9
-    traffic = read_traffic(dom, label) if profiled else None
+    traffic = read_traffic(dom, label, token_causal) if profiled else None
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
 
