@@ -79,10 +79,10 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // frames it can span (at worst alignment).
   const int HW = H * W;
   const long yx = (long)H * (3 * d / 16) + (long)W * (3 * d / 16);
-  auto rope_fits = [&](long L) {
+  auto rope_fits = [&](long L, int entries = gla::kRopeLdsEntries) {
     long frames = (L + HW - 2) / HW + 1;
     if (frames > T) frames = T;
-    return yx + frames * (d / 8) <= gla::kRopeLdsEntries;
+    return yx + frames * (d / 8) <= entries;
   };
 
   G.pass1_reg = (narrow && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
@@ -115,7 +115,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   if (token_causal) {   // one workgroup walks a whole segment
     G.cps2 = 1;
     G.chunk2 = G.seg_len;
-    G.rope_lds2 = rope_fits(G.seg_len) ? 1 : 0;
+    G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
   }
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only

@@ -32,20 +32,51 @@ struct CausalCfg {
   static constexpr int ACT = TT / TPT;                       // token groups with rows (d = 32 idles the rest)
   static constexpr int MT = D / 32;                          // 32-channel tiles
   static constexpr int PADL = Elem<L>::is_bf16 ? 8 : 4;      // elements
-  static constexpr int RP = D + PADL;                        // rqs, rks: [token][channel]
+  // bf16 operands: token-major MFMA fragments come from the row-major rk and
+  // v tiles through the LDS transpose read; fp32 operands keep transposed copies
+  static constexpr bool TR = Elem<L>::is_bf16;
+  // Row pitches (elements).  A 16-byte row read by 16 lanes (16 rows) is free
+  // of bank conflicts when the pitch is 4 (mod 8) dwords; a transpose read (32
+  // lanes: 4 rows x 64 bytes) when it is 16 (mod 64) dwords.  rq takes the
+  // first; v (transpose reads only) the second; rk, read both ways, 20 (mod 64)
+  // dwords, which keeps the row reads free and overlaps one transposed row pair.
+  static constexpr int RP = D + PADL;                        // rqs: [token][channel]
+  static constexpr int RPK = TR ? D + 40 : D + PADL;         // rks
+  static constexpr int RPV = TR ? D + 32 : D + PADL;         // vs (bf16)
   static constexpr int CP = TT + PADL;                       // rkT, vT: [channel][token]; am: [i][j]
   static constexpr int FP = D + 4;                           // zk, nums: [token][channel] fp32
   static constexpr int RQ_OFF = 0;
   static constexpr int RK_OFF = RQ_OFF + TT * RP * (int)sizeof(L);
-  static constexpr int RKT_OFF = RK_OFF + TT * RP * (int)sizeof(L);
-  static constexpr int VT_OFF = RKT_OFF + D * CP * (int)sizeof(L);
-  static constexpr int AM_OFF = VT_OFF + D * CP * (int)sizeof(L);
+  static constexpr int KT_OFF = RK_OFF + TT * RPK * (int)sizeof(L);                 // rkT [D][CP] (fp32 only)
+  static constexpr int VT_OFF = KT_OFF + (TR ? 0 : D * CP * (int)sizeof(L));         // vs [TT][RPV] or vT [D][CP]
+  static constexpr int AM_OFF = VT_OFF + (TR ? TT * RPV : D * CP) * (int)sizeof(L);
   static constexpr int ZK_OFF = AM_OFF + TT * CP * (int)sizeof(L);
   static constexpr int NUM_OFF = ZK_OFF + TT * FP * 4;
   static constexpr int SMEM = NUM_OFF + TT * FP * 4;
+  // two workgroups per CU when both fit in LDS (with the RoPE rows)
+  static constexpr int MIN_WAVES = 2 * (SMEM + kRopeLdsEntriesCausal * 8) <= 160 * 1024 ? 2 : 1;
   static_assert(TPT * ACT == TT && TPT <= 2, "token split");
   static_assert(kThreads >= D, "scan threads");
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Operand fragment of 8 consecutive tokens of one channel from a row-major
+// bf16 tile X[token][pitch] (ds_read_b64_tr_b16, two reads): lane l gets
+// channel c0 + l % 32 at tokens tok0 + 8 (l / 32) + 0..7, the MFMA layout of
+// a fragment whose K index is the token.  Within each 16-lane group, lane p
+// addresses row (p / 4) and 4-channel block (p % 4) of a 4 x 16 block; the
+// transpose hands lane i channel i of the block at the group's 4 rows.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* X, int pitch, int tok0, int c0, int lane) {
+  const int g = lane >> 4, p = lane & 15;
+  const bf16_t* a = X + (tok0 + 8 * (g >> 1) + (p >> 2)) * pitch + c0 + 16 * (g & 1) + 4 * (p & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * pitch));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 // Operand fragments in the channel order of the accumulator layout.
 template <typename L> struct PermFrag;
@@ -98,7 +129,7 @@ template <> struct BetaLoad<fp8_t> {
 };
 
 template <int D, typename E, bool LDSR>
-__global__ __launch_bounds__(kThreads) void token_causal_kernel(
+__global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_causal_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     const E* __restrict__ g, const float* __restrict__ states, const float* __restrict__ rms_w,
     const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
@@ -113,12 +144,12 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
   constexpr int TT = C::TT;
   constexpr int TPT = C::TPT;
   constexpr int SZ = D * D + D;
-  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
+  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntriesCausal * 8 : 0;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
   L* rqs = reinterpret_cast<L*>(smem + C::RQ_OFF);     // [TT][RP]  rq = R phi(q), raw q
   L* rks = reinterpret_cast<L*>(smem + C::RK_OFF);     // [TT][RP]  rk = beta R phi(k^)
-  L* rkT = reinterpret_cast<L*>(smem + C::RKT_OFF);    // [D][CP]   rk transposed
-  L* vT = reinterpret_cast<L*>(smem + C::VT_OFF);      // [D][CP]   v transposed
+  L* rkT = reinterpret_cast<L*>(smem + C::KT_OFF);     // [D][CP]   rk transposed (fp32 operands)
+  L* vT = reinterpret_cast<L*>(smem + C::VT_OFF);      // [TT][RP]  v rows (bf16) or [D][CP] v transposed
   L* am = reinterpret_cast<L*>(smem + C::AM_OFF);      // [TT][CP]  masked rk_j . rq_i, row i
   float* zk = reinterpret_cast<float*>(smem + C::ZK_OFF);    // [TT][FP] phi k^, then its running sums
   float* nums = reinterpret_cast<float*>(smem + C::NUM_OFF); // [TT][FP] numerators (token, v channel)
@@ -179,7 +210,8 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
 #pragma unroll
   for (int c = 0; c < 8; ++c) wc[c] = rms_w[8 * cg + c];
 
-  const typename R::View rv = rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  const typename R::View rv =
+      rope_view<D, LDSR, kRopeLdsEntriesCausal>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
   GridPos pos;
   pos.set((int)min(ch.begin + (long)tg * TPT, (long)G.N - 1), G.H, G.W);
   const int HW = G.H * G.W;
@@ -255,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
 #pragma unroll
         for (int c = 0; c < 8; ++c) kx[i][c] *= bt;             // rk
         L* qd = rqs + tok * C::RP + 8 * cg;
-        L* kd = rks + tok * C::RP + 8 * cg;
+        L* kd = rks + tok * C::RPK + 8 * cg;
         if constexpr (Elem<L>::is_bf16) {
           *reinterpret_cast<u32x4*>(qd) = Elem<bf16_t>::pack(rq);
           *reinterpret_cast<u32x4*>(kd) = Elem<bf16_t>::pack(kx[i]);
@@ -266,10 +298,19 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
           *reinterpret_cast<f32x4*>(kd + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
         }
       }
+      if constexpr (C::TR) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        store_tcol<L, TPT>(rkT + (8 * cg + c) * C::CP + tg * TPT, kx, c);
-        store_tcol<L, TPT>(vT + (8 * cg + c) * C::CP + tg * TPT, vx, c);
+        for (int i = 0; i < TPT; ++i) {
+          u32x4* vd = reinterpret_cast<u32x4*>(vT + (tg * TPT + i) * C::RPV + 8 * cg);
+          if constexpr (Elem<E>::is_bf16) *vd = vr[i];        // bf16 rows go to LDS as loaded
+          else *vd = Elem<bf16_t>::pack(vx[i]);               // fp8 values are exact in bf16
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          store_tcol<L, TPT>(rkT + (8 * cg + c) * C::CP + tg * TPT, kx, c);
+          store_tcol<L, TPT>(vT + (8 * cg + c) * C::CP + tg * TPT, vx, c);
+        }
       }
     }
     pos.advance(adt, ady, adx, G.H, G.W);
@@ -282,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
       f32x16 a = {};
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-        const typename M::frag fa = M::lds_frag(rks + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
+        const typename M::frag fa = M::lds_frag(rks + l32 * C::RPK + ks * M::KSTEP + M::KPL * hi);
         const typename M::frag fb = M::lds_frag(rqs + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
         a = M::mma(fa, fb, a);
       }
@@ -325,10 +366,13 @@ __global__ __launch_bounds__(kThreads) void token_causal_kernel(
       // S^T += RK^T V: A = rkT[c][j], B = vT[v][j] (v column of this wave)
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
-        vb[ks] = M::lds_frag(vT + (32 * wave + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
+        if constexpr (C::TR) vb[ks] = tr_frag(vT, C::RPV, ks * M::KSTEP, 32 * wave, lane);
+        else vb[ks] = M::lds_frag(vT + (32 * wave + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
 #pragma unroll
         for (int ct = 0; ct < C::MT; ++ct) {
-          const typename M::frag fa = M::lds_frag(rkT + (32 * ct + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
+          typename M::frag fa;
+          if constexpr (C::TR) fa = tr_frag(rks, C::RPK, ks * M::KSTEP, 32 * ct, lane);
+          else fa = M::lds_frag(rkT + (32 * ct + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
           st[ct] = M::mma(fa, vb[ks], st[ct]);
         }
       }

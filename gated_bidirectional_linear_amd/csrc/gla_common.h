@@ -85,14 +85,14 @@ __device__ __forceinline__ void store_tcol(E* dst, const float (&x)[TPT][8], int
 }
 
 // Stage the RoPE rows of the frames a chunk spans (or use the global table).
-template <int D, bool LDSR>
+template <int D, bool LDSR, int kMaxEntries = kRopeLdsEntries>
 __device__ __forceinline__ typename Rope<D>::View rope_view(float2* lds, const float2* __restrict__ rope,
                                                             const Geometry& G, long begin, long end) {
   if constexpr (LDSR) {
     const int HW = G.H * G.W;
     const int t_lo = begin < end ? (int)(begin / HW) : 0;
     const int nt = begin < end ? (int)((end - 1) / HW) - t_lo + 1 : 0;
-    return Rope<D>::template stage<kRopeLdsEntries>(lds, rope, G.T, G.H, G.W, t_lo, nt);
+    return Rope<D>::template stage<kMaxEntries>(lds, rope, G.T, G.H, G.W, t_lo, nt);
   } else {
     return typename Rope<D>::View{rope, 0, G.T, G.H};
   }

@@ -28,6 +28,8 @@ namespace gla {
 constexpr int kMaxChunks = 64;   // chunk partials per segment reduced by one tree
 constexpr int kNumKernels = 4;   // rope table, state partials, reduce/prefix, output
 constexpr int kRopeLdsEntries = 2048;  // float2 entries of RoPE table a workgroup may stage in LDS (16 KB)
+// The token-causal kernel stages fewer (14 KB) so that two workgroups fit on a CU.
+constexpr int kRopeLdsEntriesCausal = 1792;
 
 // Token partition shared by all kernels of one call.  A segment is the unit of
 // causality: the whole sequence (bidirectional) or one block of latent frames.
