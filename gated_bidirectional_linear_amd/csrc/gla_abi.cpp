@@ -37,8 +37,8 @@ int env_int(const char* name, int dflt) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Workgroups aimed for by the token-causal output kernel: one per (head,
-// segment), each walking its segment in order, one per CU at a time.
+// (head, segment) units aimed for by the token-causal walk: each is walked in
+// order by four waves; with head pairs two units share a workgroup.
 constexpr int kDefaultTargetWgTokenCausal = 512;
 constexpr int kTokenTile = 32;   // tokens per step of the token-causal kernel
 
@@ -112,15 +112,17 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   G.chunk2 = ceil_div(tiles_per_seg, cps2) * kTile;
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
-  if (token_causal) {   // one workgroup walks a whole segment
+  if (token_causal) {   // one workgroup walks a whole segment (of one head, or of a head pair)
     G.cps2 = 1;
     G.chunk2 = G.seg_len;
     G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
+    // head pairs (bf16 operands, d = 128, even head count): 512-byte row segments
+    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
   }
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
   if (!G.rope_lds1) G.pass1_reg = 0;
-  if (!G.rope_lds2) G.pass2_pair = 0;
+  if (!G.rope_lds2 && !token_causal) G.pass2_pair = 0;
   return G;
 }
 

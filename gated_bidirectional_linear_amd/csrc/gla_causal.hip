@@ -22,11 +22,12 @@ namespace gla {
 // h, register r the k channel 8(r/4) + 4h + r%4 of the lane's v column, so the
 // state enters the numerator MFMA straight from registers, with the query
 // operand read in that same channel order.
-template <int D, typename E>
+template <int D, typename E, int HP>
 struct CausalCfg {
   typedef typename Elem<E>::Lds L;
+  static constexpr int THREADS = kThreads * HP;              // four waves per head
   static constexpr int TT = 32;                              // tokens per tile
-  static constexpr int CG = D / 8;                           // 8-channel groups per token
+  static constexpr int CG = D / 8;                           // 8-channel groups per token and head
   static constexpr int TG = kThreads / CG;                   // token groups
   static constexpr int TPT = TG >= TT ? 1 : TT / TG;         // tokens per thread
   static constexpr int ACT = TT / TPT;                       // token groups with rows (d = 32 idles the rest)
@@ -52,9 +53,12 @@ struct CausalCfg {
   static constexpr int AM_OFF = VT_OFF + (TR ? TT * RPV : D * CP) * (int)sizeof(L);
   static constexpr int ZK_OFF = AM_OFF + TT * CP * (int)sizeof(L);
   static constexpr int NUM_OFF = ZK_OFF + TT * FP * 4;
-  static constexpr int SMEM = NUM_OFF + TT * FP * 4;
-  // two workgroups per CU when both fit in LDS (with the RoPE rows)
-  static constexpr int MIN_WAVES = 2 * (SMEM + kRopeLdsEntriesCausal * 8) <= 160 * 1024 ? 2 : 1;
+  static constexpr int SMEM = NUM_OFF + TT * FP * 4;        // per head
+  static constexpr int ROPE = kRopeLdsEntriesCausal * 8;
+  // waves per SIMD: a head pair's eight waves fill two; one head's four waves
+  // reach two when two workgroups fit in LDS (with the RoPE rows)
+  static constexpr int MIN_WAVES = HP == 2 ? 2 : (2 * (SMEM + ROPE) <= 160 * 1024 ? 2 : 1);
+  static_assert(HP == 1 || (HP == 2 && HP * SMEM + ROPE <= 160 * 1024), "head pair must fit in LDS");
   static_assert(TPT * ACT == TT && TPT <= 2, "token split");
   static_assert(kThreads >= D, "scan threads");
 };
@@ -76,6 +80,43 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* X, int pitch, int tok0, 
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 r = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// The 8 channels of a raw row as 4 bf16 pairs (fp8 widens exactly).
+__device__ __forceinline__ u32x4 bf16_words(const u32x4& r) { return r; }
+__device__ __forceinline__ u32x4 bf16_words(const u32x2& r) {
+  return (u32x4){Elem<fp8_t>::bf16_pair<false>(r.x), Elem<fp8_t>::bf16_pair<true>(r.x),
+                 Elem<fp8_t>::bf16_pair<false>(r.y), Elem<fp8_t>::bf16_pair<true>(r.y)};
+}
+
+// LDS copy of the RoPE rows a segment needs (frames [t_lo, t_lo + nt), then
+// the y and x blocks, laid out as the fp32 table) holding per pair the bf16
+// words (cos, -sin) and (sin, cos): each rotated channel of a ReLU'd bf16
+// pair is then one v_dot2_f32_bf16 with fp32 accumulation.
+template <int D, int kMaxEntries, int THREADS>
+__device__ __forceinline__ typename Rope<D>::View stage_rot_words(float2* lds, const float2* __restrict__ tab,
+                                                                  const Geometry& G, long begin, long end) {
+  using R = Rope<D>;
+  const int HW = G.H * G.W;
+  const int t_lo = begin < end ? (int)(begin / HW) : 0;
+  const int nt = begin < end ? (int)((end - 1) / HW) - t_lo + 1 : 0;
+  constexpr int PER = (kMaxEntries + THREADS - 1) / THREADS;
+  const int n_t = nt * R::PT;
+  const int total = n_t + G.H * R::PY + G.W * R::PX;
+  float2 tmp[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (int)threadIdx.x + j * THREADS;
+    const int src = (i < n_t) ? t_lo * R::PT + i : G.T * R::PT + (i - n_t);
+    tmp[j] = tab[i < total ? src : 0];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = (int)threadIdx.x + j * THREADS;
+    if (i < total)
+      *reinterpret_cast<u32x2*>(lds + i) = (u32x2){pack2bf(tmp[j].x, -tmp[j].y), pack2bf(tmp[j].y, tmp[j].x)};
+  }
+  return typename R::View{lds, t_lo, nt, G.H};
 }
 
 // Operand fragments in the channel order of the accumulator layout.
@@ -128,12 +169,16 @@ template <> struct BetaLoad<fp8_t> {
   __device__ __forceinline__ static float value(Raw x) { return __builtin_amdgcn_cvt_f32_fp8((int)x, 0); }
 };
 
-template <int D, typename E, bool LDSR>
-__global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_causal_kernel(
+// HP heads per workgroup (1, or 2 for bf16 operands at d = 128): with two,
+// every row load and store covers the two heads' adjacent 2 x d elements of a
+// token, which HBM serves faster than single-head segments; waves 4h..4h+3
+// own head h of the pair.
+template <int D, typename E, int HP, bool LDSR>
+__global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP>::MIN_WAVES)) void token_causal_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     const E* __restrict__ g, const float* __restrict__ states, const float* __restrict__ rms_w,
     const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
-  using C = CausalCfg<D, E>;
+  using C = CausalCfg<D, E, HP>;
   using L = typename C::L;
   using M = Mfma<L>;
   using PF = PermFrag<L>;
@@ -144,36 +189,54 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
   constexpr int TT = C::TT;
   constexpr int TPT = C::TPT;
   constexpr int SZ = D * D + D;
-  constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntriesCausal * 8 : 0;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
-  L* rqs = reinterpret_cast<L*>(smem + C::RQ_OFF);     // [TT][RP]  rq = R phi(q), raw q
-  L* rks = reinterpret_cast<L*>(smem + C::RK_OFF);     // [TT][RP]  rk = beta R phi(k^)
-  L* rkT = reinterpret_cast<L*>(smem + C::KT_OFF);     // [D][CP]   rk transposed (fp32 operands)
-  L* vT = reinterpret_cast<L*>(smem + C::VT_OFF);      // [TT][RP]  v rows (bf16) or [D][CP] v transposed
-  L* am = reinterpret_cast<L*>(smem + C::AM_OFF);      // [TT][CP]  masked rk_j . rq_i, row i
-  float* zk = reinterpret_cast<float*>(smem + C::ZK_OFF);    // [TT][FP] phi k^, then its running sums
-  float* nums = reinterpret_cast<float*>(smem + C::NUM_OFF); // [TT][FP] numerators (token, v channel)
+  constexpr int ROPE_BYTES = LDSR ? C::ROPE : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[HP * C::SMEM + ROPE_BYTES];
+  // per head h, from smem + h * SMEM:
+  //   rqs  [TT][RP]   rq = R phi(q), raw q
+  //   rks  [TT][RPK]  rk = beta R phi(k^)
+  //   rkT  [D][CP]    rk transposed (fp32 operands only)
+  //   vT   [TT][RPV]  v rows (bf16 operands) or [D][CP] v transposed
+  //   am   [TT][CP]   masked rk_j . rq_i, row i
+  //   zk   [TT][FP]   phi k^, then its running sums (fp32)
+  //   nums [TT][FP]   numerators (token, v channel), fp32
+  auto rqs = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RQ_OFF); };
+  auto rks = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RK_OFF); };
+  auto rkT = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::KT_OFF); };
+  auto vT = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::VT_OFF); };
+  auto am = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::AM_OFF); };
+  auto zk = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::ZK_OFF); };
+  auto nums = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::NUM_OFF); };
 
+  // workgroup -> (head group, segment), head groups of a segment consecutive
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
-  const Chunk ch = chunk_of(lin, G, 1, G.seg_len);
+  const int units = G.heads / HP;
+  const int seg = lin / units;
+  const int head0 = (lin - seg * units) * HP;
+  const long seg_begin = (long)seg * G.seg_len;
+  const long seg_end = min(seg_begin + (long)G.seg_len, (long)G.N);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // row work: thread = (token group, head of the pair, channel group), channels fastest
   const int cg = tid % C::CG;
-  const int tg = tid / C::CG;
+  const int hl = (tid / C::CG) % HP;
+  const int tg = tid / (C::CG * HP);
   const bool rows = tg < C::ACT;          // wave-uniform
+  // MFMA and scan work: waves 4h..4h+3 serve head h
+  const int hw = wave >> 2;
+  const int ww = wave & 3;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool incl = G.include_self != 0;
 
   const uint32_t ROW = (uint32_t)G.heads * D * sizeof(E);
-  const uint32_t head_off = (uint32_t)ch.head * D * sizeof(E);
+  const uint32_t head_off = (uint32_t)head0 * D * sizeof(E);
   const uint32_t BROW = (uint32_t)G.heads * sizeof(E);
-  const uint32_t bhead_off = (uint32_t)ch.head * sizeof(E);
-  // rows [t0, min(t0 + TT, segment end)) of this head: past them loads read 0
+  const uint32_t bhead_off = (uint32_t)head0 * sizeof(E);
+  // rows [t0, min(t0 + TT, segment end)) of these heads: past them loads read 0
   // and stores are dropped
   auto tile_rows = [&](long t0) -> uint32_t {
-    const long left = ch.end - t0;
+    const long left = seg_end - t0;
     return left <= 0 ? 0u : (left >= TT ? (uint32_t)TT : (uint32_t)left);
   };
   auto tile_rsrc = [&](const void* p, long t0) {
@@ -188,32 +251,44 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
   uint32_t voff[TPT], boff[TPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    voff[i] = (uint32_t)(tg * TPT + i) * ROW + 8u * cg * sizeof(E);
-    boff[i] = (uint32_t)(tg * TPT + i) * BROW;
+    voff[i] = (uint32_t)(tg * TPT + i) * ROW + (uint32_t)(hl * D + 8 * cg) * sizeof(E);
+    boff[i] = (uint32_t)(tg * TPT + i) * BROW + (uint32_t)hl * sizeof(E);
   }
 
-  // running state: S^T tiles of this wave's v columns, and (scan threads) z
-  const float* Sst = states + ((size_t)ch.seg * G.heads + ch.head) * SZ;
+  // running state of head hw: S^T tiles of this wave's v columns, and (scan threads) z
+  const float* Sst = states + ((size_t)seg * G.heads + head0 + hw) * SZ;
   f32x16 st[C::MT];
-  if (wave < C::MT) {
+  if (ww < C::MT) {
 #pragma unroll
     for (int ct = 0; ct < C::MT; ++ct)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sst + (size_t)(32 * wave + l32) * D + 32 * ct + 8 * rb + 4 * hi);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(Sst + (size_t)(32 * ww + l32) * D + 32 * ct + 8 * rb + 4 * hi);
         st[ct][4 * rb] = s4.x; st[ct][4 * rb + 1] = s4.y; st[ct][4 * rb + 2] = s4.z; st[ct][4 * rb + 3] = s4.w;
       }
   }
-  const int zc = tid - (kThreads - D);     // scan thread's channel
-  float zrun = zc >= 0 ? Sst[D * D + zc] : 0.f;
+  // key-sum scan: wave ww of the head takes channels 32 ww .. 32 ww + 31, lane
+  // half hi the tile's tokens 16 hi .. 16 hi + 15; both halves hold the
+  // running sum of their channel
+  const bool scanner = 32 * ww < D;
+  const int zc = 32 * ww + l32;
+  float zrun = scanner ? Sst[D * D + zc] : 0.f;
   float wc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) wc[c] = rms_w[8 * cg + c];
 
-  const typename R::View rv =
-      rope_view<D, LDSR, kRopeLdsEntriesCausal>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
+  // bf16 operands with the rows in LDS: rotation words (see stage_rot_words);
+  // otherwise fp32 (cos, sin) entries
+  constexpr bool kWords = C::TR && LDSR;
+  typename R::View rv;
+  if constexpr (kWords)
+    rv = stage_rot_words<D, kRopeLdsEntriesCausal, C::THREADS>(reinterpret_cast<float2*>(smem + HP * C::SMEM), rope,
+                                                              G, seg_begin, seg_end);
+  else
+    rv = rope_view<D, LDSR, kRopeLdsEntriesCausal>(reinterpret_cast<float2*>(smem + HP * C::SMEM), rope, G, seg_begin,
+                                                   seg_end);
   GridPos pos;
-  pos.set((int)min(ch.begin + (long)tg * TPT, (long)G.N - 1), G.H, G.W);
+  pos.set((int)min(seg_begin + (long)tg * TPT, (long)G.N - 1), G.H, G.W);
   const int HW = G.H * G.W;
   const int adt = TT / HW, ady = (TT % HW) / G.W, adx = TT % G.W;
 
@@ -235,11 +310,30 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
 #pragma unroll
     for (int i = 0; i < TPT; ++i) gr[i] = BR::load(gs, voff[i], 0);
   };
-  issue_qkvb(ch.begin);
-  issue_g(ch.begin);
+  issue_qkvb(seg_begin);
+  issue_g(seg_begin);
   if constexpr (LDSR) lds_barrier();
 
-  for (long t0 = ch.begin; t0 < ch.end; t0 += TT) {
+  // operand fragments of the previous tile's state update S^T += RK^T V, kept
+  // in registers and issued during the next tile's feature work so that the
+  // MFMAs run under vector instructions (zero before the first tile; the last
+  // tile's update is not needed: the state after the segment comes from the
+  // reduce kernel)
+  typename M::frag vb[TT / M::KSTEP], fk[C::MT][TT / M::KSTEP];
+#pragma unroll
+  for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
+    vb[ks] = typename M::frag{};
+#pragma unroll
+    for (int ct = 0; ct < C::MT; ++ct) fk[ct][ks] = typename M::frag{};
+  }
+
+  for (long t0 = seg_begin; t0 < seg_end; t0 += TT) {
+    if (ww < C::MT) {
+#pragma unroll
+      for (int ks = 0; ks < TT / M::KSTEP; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < C::MT; ++ct) st[ct] = M::mma(fk[ct][ks], vb[ks], st[ct]);
+    }
     // ---- A: token features (row layout), this tile's rows -> LDS ----------
     float phq[TPT][8], rq_scale[TPT];
     if (rows) {
@@ -252,6 +346,53 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
         cs[i] = R::fetch(rv, cg, min(pp.t, rv.t_lo + rv.nt - 1), pp.y, pp.x);
         pp.next(G.H, G.W);
       }
+      if constexpr (C::TR) {
+        // bf16 operands: RMS sums, ReLU and rotation on packed bf16 pairs
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const int tok = tg * TPT + i;
+          uint32_t wa[4], wb[4];   // (cos, -sin), (sin, cos) of pairs 0..3
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (kWords) {
+              wa[j] = __float_as_uint(cs[i].c[j]);
+              wb[j] = __float_as_uint(cs[i].s[j]);
+            } else {
+              wa[j] = pack2bf(cs[i].c[j], -cs[i].s[j]);
+              wb[j] = pack2bf(cs[i].s[j], cs[i].c[j]);
+            }
+          }
+          const u32x4 qw = bf16_words(qr[i]), kw = bf16_words(kr[i]);
+          float ssq = dot2bf(qw.x, qw.x, dot2bf(qw.y, qw.y, dot2bf(qw.z, qw.z, dot2bf(qw.w, qw.w, 0.f))));
+          float ssk = dot2bf(kw.x, kw.x, dot2bf(kw.y, kw.y, dot2bf(kw.z, kw.z, dot2bf(kw.w, kw.w, 0.f))));
+          ssq = group_sum<C::CG>(ssq);
+          ssk = group_sum<C::CG>(ssk);
+          const float msq = ssq * (1.0f / D) + G.eps;
+          rq_scale[i] = msq * __builtin_amdgcn_rsqf(msq);      // r = sqrt(mean(q^2) + eps)
+          const float inv = rsqrtf(ssk * (1.0f / D) + G.eps);
+          const float bi = BL::value(br[i]) * inv;
+          const uint32_t ql[4] = {relu2(qw.x), relu2(qw.y), relu2(qw.z), relu2(qw.w)};
+          const uint32_t kl[4] = {relu2(kw.x), relu2(kw.y), relu2(kw.z), relu2(kw.w)};
+          float rq[8], rk[8], pk[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            rq[2 * j] = dot2bf(ql[j], wa[j], 0.f);
+            rq[2 * j + 1] = dot2bf(ql[j], wb[j], 0.f);
+            rk[2 * j] = bi * dot2bf(kl[j], wa[j], 0.f);
+            rk[2 * j + 1] = bi * dot2bf(kl[j], wb[j], 0.f);
+            phq[i][2 * j] = bf16lo(ql[j]);
+            phq[i][2 * j + 1] = bf16hi(ql[j]);
+            pk[2 * j] = bf16lo(kl[j]) * inv;                // phi(k^)
+            pk[2 * j + 1] = bf16hi(kl[j]) * inv;
+          }
+          float* zrow = zk(hl) + tok * C::FP + 8 * cg;
+          *reinterpret_cast<f32x4*>(zrow) = (f32x4){pk[0], pk[1], pk[2], pk[3]};
+          *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){pk[4], pk[5], pk[6], pk[7]};
+          *reinterpret_cast<u32x4*>(rqs(hl) + tok * C::RP + 8 * cg) = Elem<bf16_t>::pack(rq);
+          *reinterpret_cast<u32x4*>(rks(hl) + tok * C::RPK + 8 * cg) = Elem<bf16_t>::pack(rk);
+          *reinterpret_cast<u32x4*>(vT(hl) + tok * C::RPV + 8 * cg) = bf16_words(vr[i]);
+        }
+      } else {
       float kx[TPT][8], vx[TPT][8];
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
@@ -279,15 +420,15 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
           rq[c] = phq[i][c];
           kx[i][c] = fmaxf(kx[i][c] * inv, 0.f);           // phi(k^)
         }
-        float* zrow = zk + tok * C::FP + 8 * cg;
+        float* zrow = zk(hl) + tok * C::FP + 8 * cg;
         *reinterpret_cast<f32x4*>(zrow) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
         *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
         R::apply(rq, cs[i]);
         R::apply(kx[i], cs[i]);
 #pragma unroll
         for (int c = 0; c < 8; ++c) kx[i][c] *= bt;             // rk
-        L* qd = rqs + tok * C::RP + 8 * cg;
-        L* kd = rks + tok * C::RPK + 8 * cg;
+        L* qd = rqs(hl) + tok * C::RP + 8 * cg;
+        L* kd = rks(hl) + tok * C::RPK + 8 * cg;
         if constexpr (Elem<L>::is_bf16) {
           *reinterpret_cast<u32x4*>(qd) = Elem<bf16_t>::pack(rq);
           *reinterpret_cast<u32x4*>(kd) = Elem<bf16_t>::pack(kx[i]);
@@ -298,19 +439,11 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
           *reinterpret_cast<f32x4*>(kd + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
         }
       }
-      if constexpr (C::TR) {
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) {
-          u32x4* vd = reinterpret_cast<u32x4*>(vT + (tg * TPT + i) * C::RPV + 8 * cg);
-          if constexpr (Elem<E>::is_bf16) *vd = vr[i];        // bf16 rows go to LDS as loaded
-          else *vd = Elem<bf16_t>::pack(vx[i]);               // fp8 values are exact in bf16
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          store_tcol<L, TPT>(rkT + (8 * cg + c) * C::CP + tg * TPT, kx, c);
-          store_tcol<L, TPT>(vT + (8 * cg + c) * C::CP + tg * TPT, vx, c);
-        }
+      for (int c = 0; c < 8; ++c) {
+        store_tcol<L, TPT>(rkT(hl) + (8 * cg + c) * C::CP + tg * TPT, kx, c);
+        store_tcol<L, TPT>(vT(hl) + (8 * cg + c) * C::CP + tg * TPT, vx, c);
+      }
       }
     }
     pos.advance(adt, ady, adx, G.H, G.W);
@@ -318,13 +451,13 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
     lds_barrier();
 
     // ---- B: masked intra-tile scores, key-sum scan, state update ------------
-    if (wave == 0) {
+    if (ww == 0) {
       // AM^T[j][i] = rk_j . rq_i on MFMA (A = RK rows, B = RQ rows), masked, stored as am[i][j]
       f32x16 a = {};
 #pragma unroll
       for (int ks = 0; ks < D / M::KSTEP; ++ks) {
-        const typename M::frag fa = M::lds_frag(rks + l32 * C::RPK + ks * M::KSTEP + M::KPL * hi);
-        const typename M::frag fb = M::lds_frag(rqs + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
+        const typename M::frag fa = M::lds_frag(rks(hw) + l32 * C::RPK + ks * M::KSTEP + M::KPL * hi);
+        const typename M::frag fb = M::lds_frag(rqs(hw) + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
         a = M::mma(fa, fb, a);
       }
 #pragma unroll
@@ -337,59 +470,71 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
           const bool keep = incl ? j <= l32 : j < l32;
           x[r] = keep ? a[4 * rb + r] : 0.f;
         }
-        L* dst = am + l32 * C::CP + j0;
+        L* dst = am(hw) + l32 * C::CP + j0;
         if constexpr (Elem<L>::is_bf16)
           *reinterpret_cast<uint2*>(dst) = make_uint2(pack2bf(x[0], x[1]), pack2bf(x[2], x[3]));
         else
           *reinterpret_cast<f32x4*>(dst) = (f32x4){x[0], x[1], x[2], x[3]};
       }
     }
-    if (zc >= 0) {
-      // running key sums z_i of this tile's tokens (inclusive or exclusive of token i)
-      float x[TT];
+    if (scanner) {
+      // running key sums z_i of this tile's tokens (inclusive or exclusive of
+      // token i): a 16-token prefix per lane half, the lower half's total
+      // handed to the upper half with v_permlane32_swap
+      constexpr int HT = TT / 2;
+      float* zcol = zk(hw) + zc + HT * hi * C::FP;
+      float p[HT];
 #pragma unroll
-      for (int j = 0; j < TT; ++j) x[j] = zk[j * C::FP + zc];
+      for (int j = 0; j < HT; ++j) p[j] = zcol[j * C::FP];
 #pragma unroll
-      for (int j = 0; j < TT; ++j) {
-        const float nxt = zrun + x[j];
-        zk[j * C::FP + zc] = incl ? nxt : zrun;
-        zrun = nxt;
+      for (int j = 1; j < HT; ++j) p[j] += p[j - 1];
+      const float tot = p[HT - 1];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+      const float lower = __uint_as_float(sw[0]);   // upper lanes: the lower half's total
+      const float upper = __uint_as_float(sw[1]);   // lower lanes: the upper half's total
+      const float base = hi ? zrun + lower : zrun;
+      if (incl) {
+#pragma unroll
+        for (int j = 0; j < HT; ++j) zcol[j * C::FP] = base + p[j];
+      } else {
+        zcol[0] = base;
+#pragma unroll
+        for (int j = 1; j < HT; ++j) zcol[j * C::FP] = base + p[j - 1];
       }
+      zrun += hi ? lower + tot : tot + upper;   // the same sum, in the same order, in both halves
     }
     typename M::frag sa[C::MT][PF::STEPS];
-    typename M::frag vb[TT / M::KSTEP];
-    if (wave < C::MT) {
+    if (ww < C::MT) {
+      // the state before this tile as operand fragments
 #pragma unroll
       for (int ct = 0; ct < C::MT; ++ct)
 #pragma unroll
         for (int s = 0; s < PF::STEPS; ++s) sa[ct][s] = PF::acc(st[ct], s);
-      // S^T += RK^T V: A = rkT[c][j], B = vT[v][j] (v column of this wave)
+      // this tile's S^T += RK^T V operands: A = rk^T[c][j], B = v[j][v] (this wave's v columns)
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
-        if constexpr (C::TR) vb[ks] = tr_frag(vT, C::RPV, ks * M::KSTEP, 32 * wave, lane);
-        else vb[ks] = M::lds_frag(vT + (32 * wave + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
+        if constexpr (C::TR) vb[ks] = tr_frag(vT(hw), C::RPV, ks * M::KSTEP, 32 * ww, lane);
+        else vb[ks] = M::lds_frag(vT(hw) + (32 * ww + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
 #pragma unroll
         for (int ct = 0; ct < C::MT; ++ct) {
-          typename M::frag fa;
-          if constexpr (C::TR) fa = tr_frag(rks, C::RPK, ks * M::KSTEP, 32 * ct, lane);
-          else fa = M::lds_frag(rkT + (32 * ct + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
-          st[ct] = M::mma(fa, vb[ks], st[ct]);
+          if constexpr (C::TR) fk[ct][ks] = tr_frag(rks(hw), C::RPK, ks * M::KSTEP, 32 * ct, lane);
+          else fk[ct][ks] = M::lds_frag(rkT(hw) + (32 * ct + l32) * C::CP + ks * M::KSTEP + M::KPL * hi);
         }
       }
     }
     lds_barrier();
 
     // ---- C: numerators on MFMA, denominators from the scanned key sums -------
-    if (wave < C::MT) {
+    if (ww < C::MT) {
       f32x16 n = {};
 #pragma unroll
       for (int ct = 0; ct < C::MT; ++ct)
 #pragma unroll
-        for (int s = 0; s < PF::STEPS; ++s) n = M::mma(sa[ct][s], PF::row(rqs + l32 * C::RP + 32 * ct, s, hi), n);
+        for (int s = 0; s < PF::STEPS; ++s) n = M::mma(sa[ct][s], PF::row(rqs(hw) + l32 * C::RP + 32 * ct, s, hi), n);
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks)
-        n = M::mma(vb[ks], M::lds_frag(am + l32 * C::CP + ks * M::KSTEP + M::KPL * hi), n);
-      float* row = nums + l32 * C::FP + 32 * wave + 4 * hi;
+        n = M::mma(vb[ks], M::lds_frag(am(hw) + l32 * C::CP + ks * M::KSTEP + M::KPL * hi), n);
+      float* row = nums(hw) + l32 * C::FP + 32 * ww + 4 * hi;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
         *reinterpret_cast<f32x4*>(row + 8 * rb) = (f32x4){n[4 * rb], n[4 * rb + 1], n[4 * rb + 2], n[4 * rb + 3]};
@@ -398,7 +543,7 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
     if (rows) {
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
-        const float* zrow = zk + (tg * TPT + i) * C::FP + 8 * cg;
+        const float* zrow = zk(hl) + (tg * TPT + i) * C::FP + 8 * cg;
         const f32x4 za = *reinterpret_cast<const f32x4*>(zrow);
         const f32x4 zb = *reinterpret_cast<const f32x4*>(zrow + 4);
         float dp = phq[i][0] * za.x + phq[i][1] * za.y + phq[i][2] * za.z + phq[i][3] * za.w +
@@ -414,7 +559,7 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
       const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
-        const float* src = nums + (tg * TPT + i) * C::FP + 8 * cg;
+        const float* src = nums(hl) + (tg * TPT + i) * C::FP + 8 * cg;
         const f32x4 a = *reinterpret_cast<const f32x4*>(src);
         const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
         float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -438,18 +583,30 @@ __global__ __launch_bounds__(kThreads, (CausalCfg<D, E>::MIN_WAVES)) void token_
   }
 }
 
+template <int D, typename E, int HP>
+static void launch_token_causal_hp(const LaunchArgs& a) {
+  const Geometry& G = a.geo;
+  const int blocks = (G.heads / HP) * G.nseg;
+  const int threads = CausalCfg<D, E, HP>::THREADS;
+  if (G.rope_lds2)
+    hipLaunchKernelGGL((token_causal_kernel<D, E, HP, true>), dim3(blocks), dim3(threads), 0, a.stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g,
+                       (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+  else
+    hipLaunchKernelGGL((token_causal_kernel<D, E, HP, false>), dim3(blocks), dim3(threads), 0, a.stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g,
+                       (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+}
+
 template <int D, typename E>
 hipError_t launch_token_causal(const LaunchArgs& a) {
-  const Geometry& G = a.geo;
-  const int blocks = G.heads * G.nseg;
-  if (G.rope_lds2)
-    hipLaunchKernelGGL((token_causal_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g, (const float*)a.states,
-                       a.rms_w, (const float2*)a.rope, (E*)a.out, G);
-  else
-    hipLaunchKernelGGL((token_causal_kernel<D, E, false>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const E*)a.g, (const float*)a.states,
-                       a.rms_w, (const float2*)a.rope, (E*)a.out, G);
+  if constexpr (D == 128 && Elem<typename Elem<E>::Lds>::is_bf16) {
+    if (a.geo.pass2_pair) {   // the planner sets it only for an even head count
+      launch_token_causal_hp<D, E, 2>(a);
+      return hipGetLastError();
+    }
+  }
+  launch_token_causal_hp<D, E, 1>(a);
   return hipGetLastError();
 }
 

@@ -357,6 +357,10 @@ __device__ __forceinline__ float dot2sq(uint32_t u, float acc) {
   const bf16x2 v = __builtin_bit_cast(bf16x2, u);
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
+// sum of the two bf16 products a.lo*b.lo + a.hi*b.hi, accumulated in fp32
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
 // ReLU of both bf16 values: the sign bit of bf16 is the int16 sign bit, and
 // int16 order matches value order on the non-negative side (v_pk_max_i16)
 __device__ __forceinline__ uint32_t relu2(uint32_t u) {

@@ -347,11 +347,6 @@ __device__ __forceinline__ uint32_t sel_channel(u32x2 ra, u32x2 rb, int c) {
 }
 
 
-// sum of the two bf16 products a.lo*b.lo + a.hi*b.hi, accumulated in fp32
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
-}
-
 // Rows [base, base + 16) of a step; rows at or past `end` read as zero.
 template <typename E>
 __device__ __forceinline__ void issue(Rows<E>& r, const E* __restrict__ k, const E* __restrict__ v,

@@ -48,17 +48,42 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
   float running = 0.f;
   if (S_in != nullptr) running = (e < D * D) ? S_in[(size_t)h * D * D + e] : z_in[(size_t)h * D + (e - D * D)];
   const float* src = partial + (size_t)h * G.nseg * G.cps1 * SZ + e;
-  for (int s = 0; s < G.nseg; ++s) {
-    float v[kMaxChunks];
+  if (G.cps1 == 1) {
+    // one partial per segment: the tree is the partial itself; the loads of
+    // 8 segments are issued together
+    constexpr int kBatch = 8;
+    for (int s0 = 0; s0 < G.nseg; s0 += kBatch) {
+      float x[kBatch];
 #pragma unroll
-    for (int i = 0; i < kMaxChunks; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
+      for (int i = 0; i < kBatch; ++i) x[i] = (s0 + i < G.nseg) ? src[(size_t)(s0 + i) * SZ] : 0.f;
 #pragma unroll
-    for (int w = kMaxChunks / 2; w >= 1; w >>= 1)
+      for (int i = 0; i < kBatch; ++i) {
+        if (s0 + i >= G.nseg) break;
+        float* dst = states + ((size_t)(s0 + i) * G.heads + h) * SZ + e;
+        if (G.states_exclusive) *dst = running;
+        running += x[i];
+        if (!G.states_exclusive) *dst = running;
+      }
+    }
+  } else {
+    // levels of the 64-leaf tree at or above the chunk count add only zeros
+    // (exactly), so they are skipped: the same sums in the same order
+    int P = 1;
+    while (P < G.cps1) P <<= 1;
+    for (int s = 0; s < G.nseg; ++s) {
+      float v[kMaxChunks];
 #pragma unroll
-      for (int i = 0; i < w; ++i) v[i] += v[i + w];
-    if (G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
-    running += v[0];
-    if (!G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
+      for (int i = 0; i < kMaxChunks; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
+#pragma unroll
+      for (int w = kMaxChunks / 2; w >= 1; w >>= 1) {
+        if (w >= P) continue;
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] += v[i + w];
+      }
+      if (G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
+      running += v[0];
+      if (!G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
+    }
   }
   if (S_out != nullptr) {
     if (e < D * D) S_out[(size_t)h * D * D + e] = running;

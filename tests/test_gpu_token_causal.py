@@ -48,6 +48,7 @@ SHAPES = [
     (3, 5, 7, 3, 64, "bf16"),
     (4, 6, 10, 4, 128, "bf16"),
     (3, 5, 7, 2, 32, "bf16"),
+    (3, 4, 6, 3, 128, "bf16"),   # odd head count: one head per workgroup
     (3, 4, 5, 2, 128, "fp8"),
     (2, 5, 9, 2, 64, "fp8"),
 ]
@@ -119,6 +120,14 @@ def test_token_causal_first_token_strict_is_zero():
     o = to_f64(out)
     assert np.all(o[0] == 0.0)
     assert np.all(np.isfinite(o))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_token_causal_one_head_kernel(monkeypatch, dtype):
+    """d = 128 with the head-pair kernel switched off: the one-head walk."""
+    monkeypatch.setenv("GLA_PASS2_GENERIC", "1")
+    inp = make_inputs(4, 5, 9, 4, 128, dtype, seed=38)
+    _check(f"tc one-head kernel {dtype}", inp, True)
 
 
 def test_token_causal_global_rope_table(monkeypatch):
