@@ -210,6 +210,10 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   if (N >= (1LL << 31)) return GLA_ERR_SHAPE;
   if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
   if (heads > (1 << 20)) return GLA_ERR_SHAPE;
+  // the kernels address up to 64 token rows of all heads through one 32-bit
+  // buffer range: a token row (heads * d elements) must stay below 2^26 bytes
+  const long long es_row = dtype == GLA_DTYPE_BF16 ? 2 : (dtype == GLA_DTYPE_FP8_E4M3 ? 1 : 4);
+  if ((long long)heads * d * es_row >= (1LL << 26)) return GLA_ERR_SHAPE;
   if (N == 0) return GLA_OK;  // nothing is read or written
   const void* ptrs[] = {q, k, v, beta, g, rms_w, out, causal ? S : rms_w, causal ? z : rms_w};
   for (const void* p : ptrs)

@@ -9,9 +9,10 @@
 
 namespace gla {
 
-// One workgroup per (head, segment) walks the segment in 32-token tiles and
-// keeps the running state transposed, S^T (k channel x v channel), in MFMA
-// accumulators: wave w owns v-channel tile w and every k-channel tile.  Per
+// Four waves per (head, segment) walk the segment in 32-token tiles (a
+// workgroup takes one head or a head pair) and keep the running state
+// transposed, S^T (k channel x v channel), in MFMA accumulators: wave w of a
+// head owns v-channel tile w and every k-channel tile.  Per
 // tile, with rq = R phi(q) (raw q; the RMS scale cancels, as in the
 // bidirectional output kernel) and rk = beta R phi(k^):
 //   num^T = S^T-as-A-operand x RQ^T      inter-tile part (state before the tile)

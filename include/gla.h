@@ -51,7 +51,8 @@ typedef enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL */
   GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, bad t_offset or include_self,
-                                 eps not finite or below FLT_MIN, size overflow */
+                                 eps not finite or below FLT_MIN, size overflow (N >= 2^31,
+                                 N*heads*d >= 2^40, or a token row heads*d*elem_size >= 2^26 bytes) */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
   GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */

@@ -126,6 +126,10 @@ def test_shape_errors(lib):
         assert fwd(lib, eps=eps) == E_SHAPE
     assert fwd(lib, T=2000, H=2000, W=2000) == E_SHAPE       # N >= 2^31
     assert fwd(lib, T=1000, H=1000, W=1000, heads=64, d=128) == E_SHAPE  # N*heads*d >= 2^40
+    # token rows of 2^26 bytes or more (heads * d * element size): the 32-bit tile ranges would overflow
+    assert fwd(lib, T=1, H=1, W=1, heads=1 << 17, d=128, dtype=0) == E_SHAPE
+    assert fwd(lib, T=1, H=1, W=1, heads=1 << 18, d=128, dtype=1) == E_SHAPE
+    assert fwd(lib, T=1, H=1, W=1, heads=(1 << 17) - 1, d=128, dtype=1, ptrs=[None] * 10) == E_NULL  # just below
     assert bc(lib, F=0) == E_SHAPE
     assert bc(lib, F=-2) == E_SHAPE
 
