@@ -101,9 +101,10 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128.  Its fp8
   // instantiation spills registers at two workgroups per CU and measured slower than the
   // one-head kernel, so fp8 keeps the one-head kernel.
+  // heads per workgroup of pass 2: pairs for bf16, d = 128 and an even head count
   G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && env_int("GLA_PASS2_GENERIC", 0) != 1)
-                     ? 1 : 0;
-  const int per_seg_units2 = G.pass2_pair ? per_seg_heads / 2 : per_seg_heads;
+                     ? 2 : 0;
+  const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
   const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", G.pass2_pair ? kDefaultTargetWgPair2 : kDefaultTargetWg2),
                              per_seg_units2);
   int cps2 = want2 < 1 ? 1 : want2;
@@ -117,7 +118,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     G.chunk2 = G.seg_len;
     G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
     // head pairs (bf16 operands, d = 128, even head count): 512-byte row segments
-    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 1 : 0;
+    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 2 : 0;
   }
   if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only

@@ -173,6 +173,12 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// x[l] + x[l ^ 16]: v_permlane16_swap hands each lane both rows of its pair
+__device__ __forceinline__ float pair_rows_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA 32x32 with fp32 accumulation.  Operand fragments per lane l:
 //   A[m = l%32][k = KPL*(l/32) + j],  B[k = KPL*(l/32) + j][n = l%32]

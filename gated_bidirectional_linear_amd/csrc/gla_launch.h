@@ -47,7 +47,9 @@ struct Geometry {
   int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
   int rope_lds2;  // same for pass 2
   int pass1_reg;  // pass 1 uses the register-accumulating kernel (bf16, d = 128, RoPE rows in LDS)
-  int pass2_pair; // pass 2 takes heads in pairs (bf16, d = 128, even heads, RoPE rows in LDS)
+  int pass2_pair; // heads per workgroup of the multi-head pass-2 kernels: 0 (one head) or 2 (bf16,
+                  // d = 128, even head count, RoPE rows in LDS; the token-causal walk takes pairs
+                  // for bf16/fp8 operands at d = 128)
   int t_offset;   // absolute frame of the call's frame 0 (RoPE positions only)
   int token_causal;   // token-level causal form: segments of seg_len tokens walked in order
   int include_self;   // token-causal: token i reads tokens j <= i (1) or j < i (0)

@@ -255,20 +255,18 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
 }
 
 // ===========================================================================
-// Fused output for bf16, d = 128, heads taken in pairs: two workgroups per CU.
+// Fused output for bf16, d = 128, HP heads per workgroup (2 or 4).
 //
-// HBM serves this op's mix of short reads and writes better when a
-// workgroup's rows are wider: with two heads per workgroup every token row
-// segment read or written is 512 contiguous bytes instead of 256 (a copy of
-// the same shape measured ~640 against ~750 us at 720p/60s).  256 threads:
-// lane group cg = tid % 32 holds 8 channels (head cg / 16, channels
-// 8 (cg % 16)..+7) of token tg = tid / 32 + 8 i (i = 0..3) of each 32-token
-// tile; rows are fetched two tiles ahead through buffer resources that end
-// at the chunk (rows past it read as zero, stores to them are dropped).  Two
-// workgroups share a CU, so one's MFMAs overlap the other's vector work.  Wave
-// w multiplies head w / 2's rotated queries by two 32-row tiles of its state
-// (16 A-fragments in registers).  The per-token math is the same as in
-// output_kernel.
+// Taking heads in pairs gives each workgroup 512-byte token row segments and
+// measured faster than one head per workgroup (~770 against ~800 us at
+// 720p/60s).  128 HP threads (two waves per head): lane group cg = tid % (16 HP)
+// holds 8 channels (head cg / 16, channels 8 (cg % 16)..+7) of token
+// tg = tid / (16 HP) + 8 i (i = 0..3) of each 32-token tile; rows are fetched
+// two tiles ahead through buffer resources that end at the chunk (rows past it
+// read as zero, stores to them are dropped).  Two workgroups share a CU, so
+// one's MFMAs overlap the other's vector work.  Wave w multiplies head w / 2's
+// rotated queries by two 32-row tiles of its state (16 A-fragments in
+// registers).  The per-token math is the same as in output_kernel.
 // ===========================================================================
 namespace pair2 {
 // 8 channels of one token as the kernel reads and writes them (bf16 rows of
@@ -285,23 +283,29 @@ template <> struct Row8<bf16_t> {
 };
 
 constexpr int D = 128;
-constexpr int HP = 2;                 // heads per workgroup
 constexpr int TILE = 32;              // tokens per tile
-constexpr int TPI = kThreads / (HP * D / 8);   // tokens per load instruction (8)
-constexpr int TPT = TILE / TPI;       // tokens per thread per tile (4)
 constexpr int DEPTH = 2;              // tiles of rows in flight
 constexpr int RQ_PITCH = D + 8;       // bf16 elements per (token, head) row
 constexpr int NUM_PITCH = D + 4;      // floats per (token, head) row
-constexpr int RQ_BYTES = TILE * HP * RQ_PITCH * 2;
-constexpr int NUM_BYTES = TILE * HP * NUM_PITCH * 4;
 constexpr int KSTEPS = D / 16;
+template <int HP>
+struct Cfg {
+  static constexpr int THREADS = 128 * HP;                 // two waves per head
+  static constexpr int LPT = HP * D / 8;                   // lanes per token row segment
+  static constexpr int TPI = THREADS / LPT;                // tokens per load instruction round (8)
+  static constexpr int TPT = TILE / TPI;                   // tokens per thread per tile (4)
+  static constexpr int RQ_BYTES = TILE * HP * RQ_PITCH * 2;
+  static constexpr int NUM_BYTES = TILE * HP * NUM_PITCH * 4;
+};
 }  // namespace pair2
 
-template <typename E>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void output_pair_kernel(
+template <typename E, int HP>
+__global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void output_pair_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ rms_w, const float2* __restrict__ rope, E* __restrict__ out, Geometry G) {
   using namespace pair2;
+  using CF = Cfg<HP>;
+  constexpr int TPI = CF::TPI, TPT = CF::TPT, RQ_BYTES = CF::RQ_BYTES, NUM_BYTES = CF::NUM_BYTES;
   using IO = Row8<E>;
   constexpr uint32_t ES = IO::ES;
   using R = Rope<D>;
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   bf16_t* rqs = reinterpret_cast<bf16_t*>(smem);                 // [TILE][HP][RQ_PITCH]
   float* nums = reinterpret_cast<float*>(smem + RQ_BYTES);       // [TILE][HP][NUM_PITCH]
 
-  // chunk-major over head pairs: consecutive ids take the same token range
+  // chunk-major over head groups: consecutive ids take the same token range
   const int npairs = G.heads / HP;
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const int ci = lin / npairs;
@@ -326,10 +330,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int cg = tid & 31;              // lane group within a token's 512 bytes
-  const int hl = cg >> 4;               // head of the pair
+  const int cg = tid % CF::LPT;         // lane group within a token's HP x 256 bytes
+  const int hl = cg >> 4;               // head within the group
   const int c16 = cg & 15;              // channels 8 c16 .. 8 c16 + 7
-  const int tg = tid >> 5;              // token within an instruction
+  const int tg = tid / CF::LPT;         // token within an instruction round
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -496,10 +500,11 @@ template <int D, typename E>
 hipError_t launch_output(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   if constexpr (D == 128 && Elem<E>::is_bf16) {
-    if (G.pass2_pair) {   // the planner sets it only for an even head count with the RoPE rows in LDS
-      hipLaunchKernelGGL((output_pair_kernel<E>), dim3((G.heads / 2) * G.nseg * G.cps2), dim3(kThreads), 0, a.stream,
-                         (const E*)a.q, (const E*)a.g, (const float*)a.states, a.rms_w,
-                         (const float2*)a.rope, (E*)a.out, G);
+    // the planner sets pass2_pair only for an even head count with the RoPE rows in LDS
+    if (G.pass2_pair == 2) {
+      hipLaunchKernelGGL((output_pair_kernel<E, 2>), dim3((G.heads / 2) * G.nseg * G.cps2),
+                         dim3(pair2::Cfg<2>::THREADS), 0, a.stream, (const E*)a.q, (const E*)a.g,
+                         (const float*)a.states, a.rms_w, (const float2*)a.rope, (E*)a.out, G);
       return hipGetLastError();
     }
   }

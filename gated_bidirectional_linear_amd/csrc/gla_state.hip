@@ -382,11 +382,6 @@ template <int I>
 __device__ __forceinline__ int row_bcast(int x) {
   return __builtin_amdgcn_mov_dpp(x, 0x150 + I, 0xF, 0xF, false);
 }
-// x[l] + x[l ^ 16]: v_permlane16_swap hands each lane both rows of its pair
-__device__ __forceinline__ float pair_rows_sum(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
 
 // The 8 operand fragments of a step: kf[c] (k side) and vf[c] (v side).
 // `offs` holds the packed table rows of this lane's own token.  The k-side

@@ -337,3 +337,16 @@ def test_one_head_output_kernel_bf16(monkeypatch, shape):
     err = rel_err(out, _oracle(inp))
     _report(f"one-head output {shape}", err, TOL["bf16"])
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(3, 22, 40, 4, 128), (4, 6, 7, 8, 128), (2, 5, 9, 6, 128), (1, 1, 1, 4, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_head_pair_output_kernel_bf16(shape):
+    """The two-heads-per-workgroup output kernel (bf16, d = 128, even head
+    counts) on several head counts and grids, down to a single token."""
+    T, H, W, heads, d = shape
+    inp = make_inputs(T, H, W, heads, d, "bf16", seed=24)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"head-pair output {shape}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
