@@ -394,64 +394,60 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
           *reinterpret_cast<u32x4*>(vT(hl) + tok * C::RPV + 8 * cg) = bf16_words(vr[i]);
         }
       } else {
-      float kx[TPT][8], vx[TPT][8];
+        // fp32 operands: fp32 features and transposed LDS copies of rk and v
+        float kx[TPT][8], vx[TPT][8];
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const int tok = tg * TPT + i;
-        float qx[8];
-        Elem<E>::unpack(qr[i], qx);
-        Elem<E>::unpack(kr[i], kx[i]);
-        Elem<E>::unpack(vr[i], vx[i]);
-        const float bt = BL::value(br[i]);
-        float ssq = 0.f, ssk = 0.f;
+        for (int i = 0; i < TPT; ++i) {
+          const int tok = tg * TPT + i;
+          float qx[8];
+          Elem<E>::unpack(qr[i], qx);
+          Elem<E>::unpack(kr[i], kx[i]);
+          Elem<E>::unpack(vr[i], vx[i]);
+          const float bt = BL::value(br[i]);
+          float ssq = 0.f, ssk = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          ssq += qx[c] * qx[c];
-          ssk += kx[i][c] * kx[i][c];
-        }
-        ssq = group_sum<C::CG>(ssq);
-        ssk = group_sum<C::CG>(ssk);
-        const float msq = ssq * (1.0f / D) + G.eps;
-        rq_scale[i] = msq * __builtin_amdgcn_rsqf(msq);      // r = sqrt(mean(q^2) + eps)
-        const float inv = rsqrtf(ssk * (1.0f / D) + G.eps);
-        float rq[8];
+          for (int c = 0; c < 8; ++c) {
+            ssq += qx[c] * qx[c];
+            ssk += kx[i][c] * kx[i][c];
+          }
+          ssq = group_sum<C::CG>(ssq);
+          ssk = group_sum<C::CG>(ssk);
+          const float msq = ssq * (1.0f / D) + G.eps;
+          rq_scale[i] = msq * __builtin_amdgcn_rsqf(msq);      // r = sqrt(mean(q^2) + eps)
+          const float inv = rsqrtf(ssk * (1.0f / D) + G.eps);
+          float rq[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          phq[i][c] = fmaxf(qx[c], 0.f);
-          rq[c] = phq[i][c];
-          kx[i][c] = fmaxf(kx[i][c] * inv, 0.f);           // phi(k^)
-        }
-        float* zrow = zk(hl) + tok * C::FP + 8 * cg;
-        *reinterpret_cast<f32x4*>(zrow) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
-        *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
-        R::apply(rq, cs[i]);
-        R::apply(kx[i], cs[i]);
+          for (int c = 0; c < 8; ++c) {
+            phq[i][c] = fmaxf(qx[c], 0.f);
+            rq[c] = phq[i][c];
+            kx[i][c] = fmaxf(kx[i][c] * inv, 0.f);           // phi(k^)
+          }
+          float* zrow = zk(hl) + tok * C::FP + 8 * cg;
+          *reinterpret_cast<f32x4*>(zrow) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
+          *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
+          R::apply(rq, cs[i]);
+          R::apply(kx[i], cs[i]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) kx[i][c] *= bt;             // rk
-        L* qd = rqs(hl) + tok * C::RP + 8 * cg;
-        L* kd = rks(hl) + tok * C::RPK + 8 * cg;
-        if constexpr (Elem<L>::is_bf16) {
-          *reinterpret_cast<u32x4*>(qd) = Elem<bf16_t>::pack(rq);
-          *reinterpret_cast<u32x4*>(kd) = Elem<bf16_t>::pack(kx[i]);
-        } else {
+          for (int c = 0; c < 8; ++c) kx[i][c] *= bt;             // rk
+          L* qd = rqs(hl) + tok * C::RP + 8 * cg;
+          L* kd = rks(hl) + tok * C::RPK + 8 * cg;
           *reinterpret_cast<f32x4*>(qd) = (f32x4){rq[0], rq[1], rq[2], rq[3]};
           *reinterpret_cast<f32x4*>(qd + 4) = (f32x4){rq[4], rq[5], rq[6], rq[7]};
           *reinterpret_cast<f32x4*>(kd) = (f32x4){kx[i][0], kx[i][1], kx[i][2], kx[i][3]};
           *reinterpret_cast<f32x4*>(kd + 4) = (f32x4){kx[i][4], kx[i][5], kx[i][6], kx[i][7]};
         }
-      }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        store_tcol<L, TPT>(rkT(hl) + (8 * cg + c) * C::CP + tg * TPT, kx, c);
-        store_tcol<L, TPT>(vT(hl) + (8 * cg + c) * C::CP + tg * TPT, vx, c);
-      }
+        for (int c = 0; c < 8; ++c) {
+          store_tcol<L, TPT>(rkT(hl) + (8 * cg + c) * C::CP + tg * TPT, kx, c);
+          store_tcol<L, TPT>(vT(hl) + (8 * cg + c) * C::CP + tg * TPT, vx, c);
+        }
       }
     }
     pos.advance(adt, ady, adx, G.H, G.W);
     issue_qkvb(t0 + TT);   // the next tile's q, k, v, beta rows (zero past the segment)
     lds_barrier();
 
-    // ---- B: masked intra-tile scores, key-sum scan, state update ------------
+    // ---- B: masked intra-tile scores, key-sum scan, state-update operands ---
     if (ww == 0) {
       // AM^T[j][i] = rk_j . rq_i on MFMA (A = RK rows, B = RQ rows), masked, stored as am[i][j]
       f32x16 a = {};
