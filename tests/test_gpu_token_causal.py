@@ -189,3 +189,27 @@ def test_token_causal_long_sequence_sampled(include_self):
                             sub["eps"], rows=np.array([0]), return_parts=True)
     assert rel_err(to_f64(S[heads]), parts["S"]) <= S_TOL["bf16"]
     assert rel_err(to_f64(z[heads]), parts["z"]) <= Z_TOL["bf16"]
+
+
+@pytest.mark.parametrize("include_self", [True, False])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_causal_single_token(dtype, include_self):
+    """One token: it reads the carried state (and itself when included)."""
+    inp = make_inputs(1, 1, 1, 2, 128, dtype, seed=39)
+    S0, z0 = make_state(2, 128, seed=5)
+    _check(f"tc single token {dtype} incl={include_self}", inp, include_self, S0, z0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_causal_large_frame_offset(dtype):
+    """Frames far into a sequence: RoPE positions t_offset + t against the
+    oracle with the same position offset, from a carried state; the offset
+    moves the oracle's output by far more than the kernel's error."""
+    T, H, W, heads, t_off = 3, 5, 6, 2, 1000
+    d = 64 if dtype == "f32" else 128
+    inp = make_inputs(T, H, W, heads, d, dtype, seed=40)
+    S0, z0 = make_state(heads, d, seed=6)
+    o = _check(f"tc frame offset {t_off} {dtype}", inp, True, S0, z0, t_offset=t_off)
+    ro, _, _ = _oracle_tc(inp, True, S0, z0, pos_offset=(t_off, 0, 0))
+    plain, _, _ = _oracle_tc(inp, True, S0, z0)
+    assert rel_err(plain, ro) > max(10 * rel_err(o, ro), TOL[dtype])
