@@ -358,7 +358,7 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the fp64 oracle on {args.cpu_heads} heads ...")
+        log(f"[bench] timing the fp64 oracle on {2 if token_causal else args.cpu_heads} heads ...")
         cpu = (cpu_baseline_token_causal(w, inp, args.form == "token-causal") if token_causal
                else cpu_baseline(w, inp, args.cpu_heads))
         log(f"[bench] oracle: {cpu['value']:.1f} tokens/s ({cpu['sample']})")
