@@ -18,8 +18,12 @@ namespace gla {
 //   num^T = S^T-as-A-operand x RQ^T      inter-tile part (state before the tile)
 //         + V^T x AM^T                   intra-tile part, AM_ij = M_ij rk_j . rq_i
 //   S^T  += RK^T x V                     state after the tile
-//   den_i = phi(q_i) . z_i + eps r_i     z_i from an fp32 scan of phi k^ over the tile
-// all on MFMA except the scan.  The accumulator layout of S^T gives lane half
+//   den_i = phi(q_i) . z_i + eps r_i     z_i = running key sum up to token i
+// For head pairs (bf16 operands) the denominator is split as the numerator is:
+// phi(q_i) . z_run (the sums before the tile, fp32, in the feature phase) plus
+// the masked row sums of phi(K^) phi(Q)^T (MFMA), and z_run grows by the
+// tile's column sums of phi(K^) (an MFMA against ones); with fp32 operands the
+// key sums are otherwise scanned in fp32.  The accumulator layout of S^T gives lane half
 // h, register r the k channel 8(r/4) + 4h + r%4 of the lane's v column, so the
 // state enters the numerator MFMA straight from registers, with the query
 // operand read in that same channel order.
@@ -52,8 +56,19 @@ struct CausalCfg {
   static constexpr int KT_OFF = RK_OFF + TT * RPK * (int)sizeof(L);                 // rkT [D][CP] (fp32 only)
   static constexpr int VT_OFF = KT_OFF + (TR ? 0 : D * CP * (int)sizeof(L));         // vs [TT][RPV] or vT [D][CP]
   static constexpr int AM_OFF = VT_OFF + (TR ? TT * RPV : D * CP) * (int)sizeof(L);
+  // Key sums.  Head pairs (bf16 operands) take the denominator's intra-tile
+  // part and the tile's key sums on MFMA from bf16 rows of phi(q) ([TT][RP])
+  // and phi(k^) ([TT][RPK]), keeping the intra-tile denominators [TT] and the
+  // tile's key sums [D] in fp32; otherwise phi(k^) is scanned in fp32
+  // ([TT][FP]), which keeps a single head's LDS small enough for two
+  // workgroups per CU.
+  static constexpr bool MD = TR && HP == 2;
   static constexpr int ZK_OFF = AM_OFF + TT * CP * (int)sizeof(L);
-  static constexpr int NUM_OFF = ZK_OFF + TT * FP * 4;
+  static constexpr int PHK_OFF = ZK_OFF + TT * RP * 2;
+  static constexpr int DIN_OFF = PHK_OFF + TT * RPK * 2;
+  static constexpr int ZS_OFF = DIN_OFF + TT * 4;
+  static constexpr int ZK_BYTES = MD ? (TT * RP + TT * RPK) * 2 + (TT + D) * 4 : TT * FP * 4;
+  static constexpr int NUM_OFF = ZK_OFF + ZK_BYTES;
   static constexpr int SMEM = NUM_OFF + TT * FP * 4;        // per head
   static constexpr int ROPE = kRopeLdsEntriesCausal * 8;
   // waves per SIMD: a head pair's eight waves fill two; one head's four waves
@@ -198,14 +213,19 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   //   rkT  [D][CP]    rk transposed (fp32 operands only)
   //   vT   [TT][RPV]  v rows (bf16 operands) or [D][CP] v transposed
   //   am   [TT][CP]   masked rk_j . rq_i, row i
-  //   zk   [TT][FP]   phi k^, then its running sums (fp32)
+  //   zk   [TT][FP]   phi k^, then its running sums (fp32 scan), or
+  //   phqs [TT][RP], phks [TT][RPK], dins [TT], zsum [D] (MFMA key sums; see CausalCfg)
   //   nums [TT][FP]   numerators (token, v channel), fp32
   auto rqs = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RQ_OFF); };
   auto rks = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RK_OFF); };
   auto rkT = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::KT_OFF); };
   auto vT = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::VT_OFF); };
   auto am = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::AM_OFF); };
-  auto zk = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::ZK_OFF); };
+  auto zk = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::ZK_OFF); };     // fp32 scan
+  auto phqs = [&](int h) { return reinterpret_cast<bf16_t*>(smem + h * C::SMEM + C::ZK_OFF); };  // MFMA key sums
+  auto phks = [&](int h) { return reinterpret_cast<bf16_t*>(smem + h * C::SMEM + C::PHK_OFF); };
+  auto dins = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::DIN_OFF); };
+  auto zsum = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::ZS_OFF); };
   auto nums = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::NUM_OFF); };
 
   // workgroup -> (head group, segment), head groups of a segment consecutive
@@ -271,9 +291,16 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   // key-sum scan: wave ww of the head takes channels 32 ww .. 32 ww + 31, lane
   // half hi the tile's tokens 16 hi .. 16 hi + 15; both halves hold the
   // running sum of their channel
-  const bool scanner = 32 * ww < D;
+  const bool scanner = !C::MD && 32 * ww < D;
   const int zc = 32 * ww + l32;
   float zrun = scanner ? Sst[D * D + zc] : 0.f;
+  // MFMA key sums: the running key sums at this thread's 8 channels of head hl
+  float zr[8];
+  {
+    const float* z0 = states + ((size_t)seg * G.heads + head0 + hl) * SZ + D * D + 8 * cg;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) zr[c] = C::MD ? z0[c] : 0.f;
+  }
   float wc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) wc[c] = rms_w[8 * cg + c];
@@ -336,7 +363,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
         for (int ct = 0; ct < C::MT; ++ct) st[ct] = M::mma(fk[ct][ks], vb[ks], st[ct]);
     }
     // ---- A: token features (row layout), this tile's rows -> LDS ----------
-    float phq[TPT][8], rq_scale[TPT];
+    float phq[TPT][8], rq_scale[TPT], dpz[TPT];
     if (rows) {
       typename R::CS cs[TPT];
       GridPos pp = pos;
@@ -386,9 +413,19 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
             pk[2 * j] = bf16lo(kl[j]) * inv;                // phi(k^)
             pk[2 * j + 1] = bf16hi(kl[j]) * inv;
           }
-          float* zrow = zk(hl) + tok * C::FP + 8 * cg;
-          *reinterpret_cast<f32x4*>(zrow) = (f32x4){pk[0], pk[1], pk[2], pk[3]};
-          *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){pk[4], pk[5], pk[6], pk[7]};
+          if constexpr (C::MD) {
+            // the denominator's part from the key sums before this tile
+            float dz = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) dz += phq[i][c] * zr[c];
+            dpz[i] = group_sum<C::CG>(dz);
+            *reinterpret_cast<u32x4*>(phqs(hl) + tok * C::RP + 8 * cg) = (u32x4){ql[0], ql[1], ql[2], ql[3]};
+            *reinterpret_cast<u32x4*>(phks(hl) + tok * C::RPK + 8 * cg) = Elem<bf16_t>::pack(pk);
+          } else {
+            float* zrow = zk(hl) + tok * C::FP + 8 * cg;
+            *reinterpret_cast<f32x4*>(zrow) = (f32x4){pk[0], pk[1], pk[2], pk[3]};
+            *reinterpret_cast<f32x4*>(zrow + 4) = (f32x4){pk[4], pk[5], pk[6], pk[7]};
+          }
           *reinterpret_cast<u32x4*>(rqs(hl) + tok * C::RP + 8 * cg) = Elem<bf16_t>::pack(rq);
           *reinterpret_cast<u32x4*>(rks(hl) + tok * C::RPK + 8 * cg) = Elem<bf16_t>::pack(rk);
           *reinterpret_cast<u32x4*>(vT(hl) + tok * C::RPV + 8 * cg) = bf16_words(vr[i]);
@@ -447,7 +484,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     issue_qkvb(t0 + TT);   // the next tile's q, k, v, beta rows (zero past the segment)
     lds_barrier();
 
-    // ---- B: masked intra-tile scores, key-sum scan, state-update operands ---
+    // ---- B: masked intra-tile scores, key sums, state-update operands -------
     if (ww == 0) {
       // AM^T[j][i] = rk_j . rq_i on MFMA (A = RK rows, B = RQ rows), masked, stored as am[i][j]
       f32x16 a = {};
@@ -472,6 +509,42 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
           *reinterpret_cast<uint2*>(dst) = make_uint2(pack2bf(x[0], x[1]), pack2bf(x[2], x[3]));
         else
           *reinterpret_cast<f32x4*>(dst) = (f32x4){x[0], x[1], x[2], x[3]};
+      }
+    }
+    if constexpr (C::MD) {
+      if (ww == 1) {
+        // intra-tile denominators: P^T[j][i] = phi(k^_j) . phi(q_i) on MFMA,
+        // masked like the scores and summed over j (16 registers, then the
+        // other lane half through v_permlane32_swap)
+        f32x16 a = {};
+#pragma unroll
+        for (int ks = 0; ks < D / M::KSTEP; ++ks) {
+          const typename M::frag fa = M::lds_frag(phks(hw) + l32 * C::RPK + ks * M::KSTEP + M::KPL * hi);
+          const typename M::frag fb = M::lds_frag(phqs(hw) + l32 * C::RP + ks * M::KSTEP + M::KPL * hi);
+          a = M::mma(fa, fb, a);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool keep = incl ? j <= l32 : j < l32;
+          part += keep ? a[r] : 0.f;
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        if (hi == 0) dins(hw)[l32] = part + __uint_as_float(sw[1]);
+      } else if (ww == 2) {
+        // the tile's key sums per channel: ones x phi(K^) on MFMA (every row of
+        // the product holds the column sums)
+        const uint4 ones4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
+        const typename M::frag ones = __builtin_bit_cast(bf16x8, ones4);
+#pragma unroll
+        for (int ct = 0; ct < C::MT; ++ct) {
+          f32x16 a = {};
+#pragma unroll
+          for (int ks = 0; ks < TT / M::KSTEP; ++ks)
+            a = M::mma(ones, tr_frag(phks(hw), C::RPK, ks * M::KSTEP, 32 * ct, lane), a);
+          if (hi == 0) zsum(hw)[32 * ct + l32] = a[0];
+        }
       }
     }
     if (scanner) {
@@ -521,7 +594,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     }
     lds_barrier();
 
-    // ---- C: numerators on MFMA, denominators from the scanned key sums -------
+    // ---- C: numerators on MFMA, denominators --------------------------------
     if (ww < C::MT) {
       f32x16 n = {};
 #pragma unroll
@@ -538,15 +611,26 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     }
     float rden[TPT];
     if (rows) {
+      if constexpr (C::MD) {
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) {
-        const float* zrow = zk(hl) + (tg * TPT + i) * C::FP + 8 * cg;
-        const f32x4 za = *reinterpret_cast<const f32x4*>(zrow);
-        const f32x4 zb = *reinterpret_cast<const f32x4*>(zrow + 4);
-        float dp = phq[i][0] * za.x + phq[i][1] * za.y + phq[i][2] * za.z + phq[i][3] * za.w +
-                   phq[i][4] * zb.x + phq[i][5] * zb.y + phq[i][6] * zb.z + phq[i][7] * zb.w;
-        dp = group_sum<C::CG>(dp);
-        rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * rq_scale[i]);
+        for (int i = 0; i < TPT; ++i)
+          rden[i] = __builtin_amdgcn_rcpf(dpz[i] + dins(hl)[tg * TPT + i] + G.eps * rq_scale[i]);
+        // running key sums after this tile
+        const f32x4 za = *reinterpret_cast<const f32x4*>(zsum(hl) + 8 * cg);
+        const f32x4 zb = *reinterpret_cast<const f32x4*>(zsum(hl) + 8 * cg + 4);
+        zr[0] += za.x; zr[1] += za.y; zr[2] += za.z; zr[3] += za.w;
+        zr[4] += zb.x; zr[5] += zb.y; zr[6] += zb.z; zr[7] += zb.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const float* zrow = zk(hl) + (tg * TPT + i) * C::FP + 8 * cg;
+          const f32x4 za = *reinterpret_cast<const f32x4*>(zrow);
+          const f32x4 zb = *reinterpret_cast<const f32x4*>(zrow + 4);
+          float dp = phq[i][0] * za.x + phq[i][1] * za.y + phq[i][2] * za.z + phq[i][3] * za.w +
+                     phq[i][4] * zb.x + phq[i][5] * zb.y + phq[i][6] * zb.z + phq[i][7] * zb.w;
+          dp = group_sum<C::CG>(dp);
+          rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * rq_scale[i]);
+        }
       }
     }
     lds_barrier();
