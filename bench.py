@@ -141,11 +141,27 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
         print(f"wrote {path}: {(fetched + written) / 1e9:.3f} GB per launch")
 
 
-def write_stats_summary(stats_csv: str, workload: str, commands: str, token_causal: bool = False) -> None:
+def write_stats_summary(stats_csv: str, workload: str, commands: str, token_causal: bool = False,
+                        warmup: int = 2, bench_log: str = "") -> None:
     """Kernel-trace statistics (rocprofv3 --kernel-trace --stats, kernel_stats.csv)
-    as a short text table under profiles/."""
+    as a short text table under profiles/, plus, from the per-dispatch trace
+    next to it (kernel_trace.csv), each kernel's mean over the launches after
+    the first `warmup` calls (the timed steps of the profiled command), and the
+    HIP-event times per launch that the profiled bench.py run itself printed
+    (its JSON line in `bench_log`)."""
+    import collections
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    steady = {}
+    if os.path.exists(trace_csv):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        for k, v in per.items():
+            v.sort()
+            timed = v[warmup:] if len(v) > warmup else v
+            steady[k] = (sum(e - b for b, e in timed) / len(timed) / 1e3, len(timed))
     path = os.path.join(ROOT, "profiles", f"kernels_{workload}_stats.txt")
     with open(path, "w") as f:
         f.write(f"# rocprofv3 kernel-trace statistics, {workload} workload\n")
@@ -157,6 +173,23 @@ def write_stats_summary(stats_csv: str, workload: str, commands: str, token_caus
             name = r["Name"].split("(")[0].replace("void ", "")
             f.write(f"{name[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
                     f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}\n")
+        if steady:
+            f.write(f"# mean over the timed steps (launches after the first {warmup}), from the per-dispatch trace:\n")
+            for k, (us, n) in sorted(steady.items(), key=lambda kv: -kv[1][0]):
+                if n <= 1:
+                    continue
+                name = k.split("(")[0].replace("void ", "")
+                f.write(f"steady {name[:53]:53s} {n:6d} {us:10.1f}\n")
+        if bench_log and os.path.exists(bench_log):
+            rec = None
+            for line in open(bench_log):
+                if line.startswith("{"):
+                    rec = json.loads(line)
+            if rec is not None:
+                f.write("# the same run's own HIP-event times per launch (bench.py JSON line):\n")
+                for k, v in rec.get("kernels", {}).items():
+                    if v.get("ms_per_launch"):
+                        f.write(f"events {k:53s} {v['launches']:6d} {v['ms_per_launch'] * 1e3:10.1f}\n")
         f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
     print(f"wrote {path}")
 
@@ -248,12 +281,14 @@ def main(argv=None):
                     help="CPU only: write the kernel-trace summary under profiles/ from a rocprofv3 "
                          "kernel_stats.csv")
     ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
+    ap.add_argument("--stats-bench-log", default="", help="output of the profiled bench.py run (its JSON line)")
     args = ap.parse_args(argv)
 
     token_causal = args.form != "workload"
     label = args.workload + ("_token_causal" if token_causal else "")   # names the profiles/ summaries
     if args.stats_summary:
-        write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal)
+        write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal, args.warmup,
+                            args.stats_bench_log)
         return 0
     if args.pmc_summary:
         write_traffic_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024,
