@@ -27,6 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}   # dense MFMA of the operand type the kernels use
+# (fp8 I/O is widened to bf16 operands; fp32 I/O runs fp32 MFMA)
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
 KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
                   ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
@@ -56,6 +58,18 @@ def kernel_alg_bytes(w, kernel: str, token_causal: bool = False) -> int:
         return 3 * big
     if kernel == "state_partial_kernel":  # read k, v, beta
         return 2 * big + w.N * w.heads * s
+    return 0
+
+
+def kernel_alg_flops(w, kernel: str, token_causal: bool = False) -> int:
+    """Algorithmic MFMA flops of one launch: the state contraction (pass 1)
+    and the numerators (pass 2), 2 N heads d^2 each; the token-causal walk
+    does both (its intra-tile products are design overhead, not counted)."""
+    one = 2 * w.N * w.heads * w.d * w.d
+    if kernel == "output_kernel":
+        return 2 * one if token_causal else one
+    if kernel == "state_partial_kernel":
+        return one
     return 0
 
 
@@ -139,6 +153,44 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
             f.write(f"traffic_bytes_per_launch: {fetched + written:.0f}\n")
             f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
         print(f"wrote {path}: {(fetched + written) / 1e9:.3f} GB per launch")
+
+
+def write_mfma_summary(pmc_csv: str, workload: str, commands: str, token_causal: bool = False,
+                       num_cu: int = 256, num_xcd: int = 8) -> None:
+    """MFMA busy fraction per kernel from a rocprofv3 counter run of
+    SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over every SIMD: 32 per
+    32x32x16 bf16 MFMA) and GRBM_GUI_ACTIVE (active cycles summed over the
+    XCDs): busy / (GRBM_GUI_ACTIVE / XCDs x CUs x 4 SIMDs).  The active cycles
+    over the dispatch's duration give the clock the kernel ran at."""
+    import collections
+    import csv
+    busy = _pmc_means(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
+    active = _pmc_means(pmc_csv, "GRBM_GUI_ACTIVE")
+    dur = collections.defaultdict(list)
+    seen = set()
+    for r in csv.DictReader(open(pmc_csv)):
+        if r["Dispatch_Id"] in seen:
+            continue
+        seen.add(r["Dispatch_Id"])
+        dur[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.txt")
+    with open(path, "w") as f:
+        f.write(f"# MFMA busy fraction per kernel on the {workload} workload, from rocprofv3 counters\n")
+        f.write("# commands:\n")
+        for line in commands.strip().splitlines():
+            f.write(f"#   {line}\n")
+        f.write(f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {num_xcd} XCDs x {num_cu} CUs x 4 SIMDs);\n")
+        f.write("# clock = GRBM_GUI_ACTIVE / XCDs / dispatch duration (means over dispatches)\n")
+        for k in sorted(busy):
+            if not k.removeprefix("void ").startswith("gla::") or not active.get(k):
+                continue
+            cycles = active[k] / num_xcd
+            frac = busy[k] / (cycles * num_cu * 4)
+            ns = sum(dur[k]) / len(dur[k]) if dur.get(k) else 0.0
+            clock = f"{cycles / ns:5.2f} GHz" if ns > 50_000 else "n/a (short dispatch)"
+            f.write(f"{k.removeprefix('void ').split('(')[0][:60]:60s} mfma_busy {frac:7.4f}  clock {clock}\n")
+        f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
+    print(f"wrote {path}")
 
 
 def write_stats_summary(stats_csv: str, workload: str, commands: str, token_causal: bool = False,
@@ -282,10 +334,16 @@ def main(argv=None):
                          "kernel_stats.csv")
     ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
     ap.add_argument("--stats-bench-log", default="", help="output of the profiled bench.py run (its JSON line)")
+    ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
+                    help="CPU only: write the MFMA busy summary under profiles/ from a rocprofv3 "
+                         "counter_collection.csv of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     args = ap.parse_args(argv)
 
     token_causal = args.form != "workload"
     label = args.workload + ("_token_causal" if token_causal else "")   # names the profiles/ summaries
+    if args.mfma_summary:
+        write_mfma_summary(args.mfma_summary, label, args.pmc_commands, token_causal)
+        return 0
     if args.stats_summary:
         write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal, args.warmup,
                             args.stats_bench_log)
@@ -436,6 +494,12 @@ def main(argv=None):
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
         },
+        "mfma": {k: {
+            "achieved": kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12,
+            "peak": MFMA_PEAK_TFLOPS[w.dtype],
+            "unit": "TFLOP/s",
+            "frac": kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+        } for k in ("state_partial_kernel", "output_kernel") if kt[k][1]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
