@@ -484,7 +484,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     issue_qkvb(t0 + TT);   // the next tile's q, k, v, beta rows (zero past the segment)
     lds_barrier();
 
-    // ---- B: masked intra-tile scores, key sums, state-update operands -------
+    // ---- B: masked intra-tile scores, key sums, inter-tile numerators -------
     if (ww == 0) {
       // AM^T[j][i] = rk_j . rq_i on MFMA (A = RK rows, B = RQ rows), masked, stored as am[i][j]
       f32x16 a = {};
@@ -573,13 +573,15 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
       }
       zrun += hi ? lower + tot : tot + upper;   // the same sum, in the same order, in both halves
     }
-    typename M::frag sa[C::MT][PF::STEPS];
+    f32x16 n = {};   // num^T of this wave's v tile
     if (ww < C::MT) {
-      // the state before this tile as operand fragments
+      // inter-tile numerators: the state before this tile, as operand
+      // fragments, times RQ^T (independent of the scores, so issued here)
 #pragma unroll
       for (int ct = 0; ct < C::MT; ++ct)
 #pragma unroll
-        for (int s = 0; s < PF::STEPS; ++s) sa[ct][s] = PF::acc(st[ct], s);
+        for (int s = 0; s < PF::STEPS; ++s)
+          n = M::mma(PF::acc(st[ct], s), PF::row(rqs(hw) + l32 * C::RP + 32 * ct, s, hi), n);
       // this tile's S^T += RK^T V operands: A = rk^T[c][j], B = v[j][v] (this wave's v columns)
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
@@ -594,13 +596,8 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     }
     lds_barrier();
 
-    // ---- C: numerators on MFMA, denominators --------------------------------
+    // ---- C: intra-tile numerators on MFMA, denominators ----------------------
     if (ww < C::MT) {
-      f32x16 n = {};
-#pragma unroll
-      for (int ct = 0; ct < C::MT; ++ct)
-#pragma unroll
-        for (int s = 0; s < PF::STEPS; ++s) n = M::mma(sa[ct][s], PF::row(rqs(hw) + l32 * C::RP + 32 * ct, s, hi), n);
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks)
         n = M::mma(vb[ks], M::lds_frag(am(hw) + l32 * C::CP + ks * M::KSTEP + M::KPL * hi), n);
