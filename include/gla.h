@@ -38,7 +38,9 @@
  * identical inputs and shapes.  On any error nothing is enqueued and no
  * output is written.  Temporary device memory (RoPE tables, per-chunk partial
  * states) is taken stream-ordered from the device's default memory pool and
- * returned on the same stream.
+ * returned on the same stream.  A call may be captured into a HIP graph (it
+ * records kernels and stream-ordered allocations only, no memset nodes);
+ * replays recompute it.
  */
 #ifndef GLA_H
 #define GLA_H
