@@ -7,19 +7,23 @@
 //   o_j = w * rmsnorm( sigmoid(g_j) * (S R_j phi q^_j) / (phi q^_j . z + eps) )
 //
 // The tokens are cut into "segments": one segment of N tokens for the
-// bidirectional form, or one per block of latent frames for the block-causal
+// bidirectional form, one per block of latent frames for the block-causal
+// form, or runs of 32-token tiles sized for parallelism in the token-causal
 // form.  Four launches on the caller's stream:
 //   1. rope_table_kernel    (gla_tables.hip): per-axis cos/sin tables, fp64 angles.
 //   2. state_partial kernels (gla_state.hip): one workgroup per (head, chunk of
 //      a segment) builds the partial V^T (beta R phi K^) on MFMA with fp32
 //      accumulation, plus the partial key sum.
 //   3. state_reduce_kernel  (gla_tables.hip): fixed-shape pairwise tree over the
-//      chunk partials of each segment, then an inclusive prefix over segments
-//      on top of the carried state -> per-segment states.
-//   4. output_kernel        (gla_output.hip): one workgroup per (head, chunk of
-//      tiles) holds its slice of S as MFMA A-fragments, streams q and g,
-//      computes num^T = S RQ^T on MFMA, the denominator, gate and RMSNorm, and
-//      writes the output once.
+//      chunk partials of each segment, then a prefix over segments on top of
+//      the carried state -> per-segment states (inclusive of the segment, or
+//      exclusive for the token-causal form) and the state after the call.
+//   4. output_kernel        (gla_output.hip): one workgroup per (head or head
+//      pair, chunk of tiles) holds its slice of S as MFMA A-fragments, streams
+//      q and g, computes num^T = S RQ^T on MFMA, the denominator, gate and
+//      RMSNorm, and writes the output once; or, in the token-causal form,
+//      token_causal_kernel (gla_causal.hip), which walks each segment from its
+//      exclusive state.
 #pragma once
 #include <hip/hip_runtime_api.h>
 
