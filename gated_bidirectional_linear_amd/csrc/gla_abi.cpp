@@ -25,7 +25,8 @@ constexpr int kDefaultTargetWg1 = 512;
 // one workgroup per CU.
 constexpr int kDefaultTargetWgAcc1 = 256;
 constexpr int kDefaultTargetWg2 = 2048;
-// The paired-head output kernel (bf16, d = 128) runs two workgroups per CU.
+// The paired-head output kernel (bf16, d = 128) runs two workgroups per CU
+// (720p/60s in the full step: 722 us at 1024, 740 us at 3072).
 constexpr int kDefaultTargetWgPair2 = 1024;
 
 int env_int(const char* name, int dflt) {

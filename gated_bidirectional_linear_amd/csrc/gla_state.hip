@@ -239,10 +239,7 @@ constexpr int kOffBits = 10;                   // packed table row offset (16-by
 constexpr int kRotBytes = kRopeLdsEntries * 8; // LDS rotation table
 using R = Rope<D>;
 
-// Streaming loads carry the nontemporal hint (bit 1 of the cache-policy
-// operand): every row is read once.
-constexpr int kStreamPolicy = 2;
-
+// Every row is read once: streaming loads carry kLoadStream (nontemporal).
 // The tensor element type seen by the bf16 code: 4 channels of one token as
 // two bf16 words.  fp8 rows are loaded as 4 bytes and widened right before
 // use (every e4m3 value is exact in bf16).
@@ -251,7 +248,7 @@ template <> struct Io<bf16_t> {
   static constexpr uint32_t ES = 2;   // bytes per element
   typedef u32x2 Word;                 // 4 channels as loaded
   __device__ __forceinline__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kStreamPolicy));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kLoadStream));
   }
   __device__ __forceinline__ static u32x2 bf16x4(Word w) { return w; }
   __device__ __forceinline__ static uint32_t load_beta(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
@@ -263,7 +260,7 @@ template <> struct Io<fp8_t> {
   static constexpr uint32_t ES = 1;
   typedef uint32_t Word;
   __device__ __forceinline__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kStreamPolicy);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kLoadStream);
   }
   __device__ __forceinline__ static u32x2 bf16x4(Word w) {
     return (u32x2){Elem<fp8_t>::bf16_pair<false>(w), Elem<fp8_t>::bf16_pair<true>(w)};
