@@ -242,10 +242,13 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   const int cg = tid % C::CG;
   const int hl = (tid / C::CG) % HP;
   const int tg = tid / (C::CG * HP);
-  const bool rows = tg < C::ACT;          // wave-uniform
+  // wave-uniform; true for every thread unless d = 32 (stated as a constant
+  // then, so that the phases' row work and MFMAs share basic blocks)
+  const bool rows = C::ACT * C::CG * HP == C::THREADS || tg < C::ACT;
   // MFMA and scan work: waves 4h..4h+3 serve head h
   const int hw = wave >> 2;
   const int ww = wave & 3;
+  const bool mt_wave = C::MT >= 4 || ww < C::MT;   // this wave owns a 32-column tile of S^T
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool incl = G.include_self != 0;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   // running state of head hw: S^T tiles of this wave's v columns, and (scan threads) z
   const float* Sst = states + ((size_t)seg * G.heads + head0 + hw) * SZ;
   f32x16 st[C::MT];
-  if (ww < C::MT) {
+  if (mt_wave) {
 #pragma unroll
     for (int ct = 0; ct < C::MT; ++ct)
 #pragma unroll
@@ -356,7 +359,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   }
 
   for (long t0 = seg_begin; t0 < seg_end; t0 += TT) {
-    if (ww < C::MT) {
+    if (mt_wave) {
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks)
 #pragma unroll
@@ -574,7 +577,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
       zrun += hi ? lower + tot : tot + upper;   // the same sum, in the same order, in both halves
     }
     f32x16 n = {};   // num^T of this wave's v tile
-    if (ww < C::MT) {
+    if (mt_wave) {
       // inter-tile numerators: the state before this tile, as operand
       // fragments, times RQ^T (independent of the scores, so issued here)
 #pragma unroll
@@ -594,10 +597,24 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
         }
       }
     }
+    // the gate sigmoid(g) of this tile's rows, computed here where the vector
+    // unit would otherwise wait on the numerator MFMAs; the g registers are
+    // then free for the next tile's rows
+    float sig[TPT][8];
+    if (rows) {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        float gv[8];
+        Elem<E>::unpack(gr[i], gv);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sig[i][c] = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));
+      }
+    }
+    issue_g(t0 + TT);
     lds_barrier();
 
     // ---- C: intra-tile numerators on MFMA, denominators ----------------------
-    if (ww < C::MT) {
+    if (mt_wave) {
 #pragma unroll
       for (int ks = 0; ks < TT / M::KSTEP; ++ks)
         n = M::mma(vb[ks], M::lds_frag(am(hw) + l32 * C::CP + ks * M::KSTEP + M::KPL * hi), n);
@@ -641,12 +658,10 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
         const f32x4 a = *reinterpret_cast<const f32x4*>(src);
         const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
         float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        float gv[8];
-        Elem<E>::unpack(gr[i], gv);
         float ss = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));
+          y[c] *= sig[i][c];
           ss += y[c] * y[c];
         }
         ss = group_sum<C::CG>(ss);
@@ -657,7 +672,6 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
         BR::store(ors, voff[i], 0, Elem<E>::pack(y));
       }
     }
-    issue_g(t0 + TT);
   }
 }
 
