@@ -178,7 +178,10 @@ int gla_version(void);
  * into launches[i] for kernel i < min(n, GLA_NUM_KERNELS), then clears the
  * record.  Kernel ids: 0 RoPE table, 1 state partials, 2 state reduce/prefix,
  * 3 fused output.  Timing is process-wide and not thread-safe; turning it on
- * adds event records to every call.  Returns GLA_OK or GLA_ERR_HIP.
+ * adds event records to every call.  The events are timing-only (no
+ * system-scope fence when they complete): waiting on them through
+ * gla_timing_read does not make the calls' outputs visible to the host; the
+ * caller still synchronises the stream for that.  Returns GLA_OK or GLA_ERR_HIP.
  */
 #define GLA_NUM_KERNELS 4
 int gla_timing_enable(int on);
