@@ -3,11 +3,13 @@ e4m3fn; fp32 state and accumulation) against the fp64 oracle evaluated on the
 exact decoded fp8 inputs.  The output is compared beyond its own rounding:
 |got - ref| - 2^-4 |ref| - 2^-10 <= 2e-2 max|ref| (the bf16 tolerance for the
 path's internal error)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
 import oracle.gla_oracle as orc
-from workloads import WORKLOADS, make_inputs, make_state
+from workloads import WORKLOADS, head_slice_f32, make_inputs, make_state, make_workload_inputs
 from tests.gpu_helpers import TOL, Z_TOL, fp8_excess, rel_err, run_block_causal, run_forward, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +52,27 @@ def test_fp8_480p_workload():
     got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
     err = fp8_excess(got, _oracle(inp))
     _report(w.name, err)
+    assert err <= TOL["fp8"]
+
+
+def test_fp8_long_sequence_sampled():
+    """720p/60s with fp8 I/O at full size (N = 159,280, 32 heads; the launch
+    plan the fp8 bench line times): the oracle evaluates 3 heads at 1,024
+    sampled tokens from the decoded fp8 inputs of those heads."""
+    torch = pytest.importorskip("torch")
+    w = dataclasses.replace(WORKLOADS["720p_60s"], dtype="fp8")
+    print(f"[case] fp8 {w.name} N={w.N} heads={w.heads}", flush=True)
+    inp = make_workload_inputs(w, seed=0, keep_f32=False)
+    out = run_forward(to_device(inp), inp["grid"], inp["eps"])
+    assert bool(torch.isfinite(out.float()).all())
+    rng = np.random.default_rng(124)
+    rows = np.unique(np.concatenate([[0, 1, w.N - 1], rng.integers(0, w.N, 1021)]))
+    heads = [0, 13, 31]
+    sub = head_slice_f32(inp, heads)
+    ref = _oracle(sub, rows=rows)
+    got = to_f64(out[torch.from_numpy(rows).cuda()][:, heads, :])
+    err = fp8_excess(got, ref)
+    _report(w.name + " sampled", err)
     assert err <= TOL["fp8"]
 
 
