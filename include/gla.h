@@ -35,10 +35,17 @@
  * `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  * are asynchronous: they validate on the host, enqueue kernels on `stream`
  * and return; the caller synchronises.  Results are bitwise reproducible for
- * identical inputs and shapes.  On any error nothing is enqueued and no
- * output is written.  Temporary device memory (RoPE tables, per-chunk partial
- * states) is taken stream-ordered from the device's default memory pool and
- * returned on the same stream.  A call may be captured into a HIP graph (it
+ * identical inputs and shapes.  On a validation error (any status other than
+ * GLA_ERR_HIP and GLA_ERR_ALLOC) nothing is enqueued and nothing is written;
+ * GLA_ERR_ALLOC also enqueues nothing.  GLA_ERR_HIP means a kernel launch
+ * failed after the call's earlier kernels were enqueued: the output is then
+ * undefined, and in the causal forms the carried state may already hold the
+ * state after the call.  Temporary device memory (RoPE tables, per-chunk
+ * partial states) is taken stream-ordered from the device's default memory
+ * pool and returned on the same stream; on its first call on a device the
+ * library raises that pool's release threshold to the maximum, so that freed
+ * scratch stays cached between calls (a setting of the process's default
+ * pool, seen by its other users).  A call may be captured into a HIP graph (it
  * records kernels and stream-ordered allocations only, no memset nodes);
  * replays recompute it.
  */
