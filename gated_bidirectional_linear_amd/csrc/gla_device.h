@@ -374,6 +374,18 @@ __device__ __forceinline__ float dot2sq(uint32_t u, float acc) {
   const bf16x2 v = __builtin_bit_cast(bf16x2, u);
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
+// Gates read as fp8 e4m3 take sigmoid(g) from a table of all 256 codes in
+// LDS: one read per element in place of a decode, an exp and a reciprocal.
+// The entries use the per-element formula, so the results are the same.
+__device__ __forceinline__ void fill_sigmoid_fp8(float* tab, int tid, int nthreads) {
+  for (int i = tid; i < 256; i += nthreads)
+    tab[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-__builtin_amdgcn_cvt_f32_fp8(i, 0)));
+}
+// sigmoid of code `byte` (0..3) of the packed word w
+__device__ __forceinline__ float sigmoid_fp8(const float* tab, uint32_t w, int byte) {
+  return tab[(w >> (8 * byte)) & 0xffu];
+}
+
 // sum of the two bf16 products a.lo*b.lo + a.hi*b.hi, accumulated in fp32
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);

@@ -51,7 +51,9 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   constexpr int SZ = D * D + D;
   constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
   constexpr bool kBf16 = Elem<E>::is_bf16;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES];
+  constexpr bool kFp8 = sizeof(E) == 1;
+  constexpr int SIG_BYTES = kFp8 ? 256 * 4 : 0;   // sigmoid of every fp8 gate code
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES + SIG_BYTES];
   constexpr int kT = C::TILE;
   L* rqs = reinterpret_cast<L*>(smem);                          // [kT][RQ_PITCH]  (token, k channel)
   float* nums = reinterpret_cast<float*>(smem + C::RQ_BYTES);   // [kT][NUM_PITCH] (token, v channel)
@@ -65,6 +67,9 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   const int tg = tid / C::CG;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  // read first in a tile's epilogue, after that tile's two barriers
+  float* sig_tab = reinterpret_cast<float*>(smem + C::SMEM + ROPE_BYTES);
+  if constexpr (kFp8) fill_sigmoid_fp8(sig_tab, tid, kThreads);
 
   // Every tile's loads and stores go through buffer resources based at the
   // tile's first row and this head and ending at the chunk's last row: rows
@@ -223,13 +228,21 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       const f32x4 a = *reinterpret_cast<const f32x4*>(src);
       const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
       float y[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      float gv[8];
-      Elem<E>::unpack(gr[i], gv);
       float ss = 0.f;
+      if constexpr (kFp8) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));   // sigmoid(g) * num
-        ss += y[c] * y[c];
+        for (int c = 0; c < 8; ++c) {
+          y[c] *= sigmoid_fp8(sig_tab, c < 4 ? gr[i].x : gr[i].y, c & 3);   // sigmoid(g) * num
+          ss += y[c] * y[c];
+        }
+      } else {
+        float gv[8];
+        Elem<E>::unpack(gr[i], gv);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          y[c] *= __builtin_amdgcn_rcpf(1.0f + __expf(-gv[c]));   // sigmoid(g) * num
+          ss += y[c] * y[c];
+        }
       }
       ss = group_sum<C::CG>(ss);
       const float rd = rden[i];
