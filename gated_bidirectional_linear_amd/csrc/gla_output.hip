@@ -170,7 +170,10 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           ss += ph[c] * ph[c];
-          ph[c] = fmaxf(ph[c], 0.f);
+          // ReLU as one v_max_i32 on the bits (fmaxf adds a canonicalising max):
+          // every negative value, -0 included, has the sign bit set
+          const int b = __float_as_int(ph[c]);
+          ph[c] = __int_as_float(b > 0 ? b : 0);
         }
       }
       float dp = 0.f;
