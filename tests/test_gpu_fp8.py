@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.gla_oracle as orc
-from workloads import WORKLOADS, head_slice_f32, make_inputs, make_state, make_workload_inputs
+from workloads import WORKLOADS, fp8_bits_to_f32, head_slice_f32, make_inputs, make_state, make_workload_inputs
 from tests.gpu_helpers import TOL, Z_TOL, fp8_excess, rel_err, run_block_causal, run_forward, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -73,6 +73,26 @@ def test_fp8_long_sequence_sampled():
     got = to_f64(out[torch.from_numpy(rows).cuda()][:, heads, :])
     err = fp8_excess(got, ref)
     _report(w.name + " sampled", err)
+    assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_every_gate_code(d):
+    """Gates running through every finite e4m3 code (both signs, subnormals up
+    to +-448, the two NaN codes left out), so the gate's sigmoid is checked at
+    every input the format has, saturated ends included."""
+    T, H, W, heads = 4, 8, 9, 2
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=41)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    n = inp["g_bits"].size
+    bits = np.resize(np.random.default_rng(5).permutation(codes), n).reshape(inp["g_bits"].shape)
+    inp["g_bits"] = bits
+    inp["g"] = fp8_bits_to_f32(bits)
+    assert set(np.unique(bits)) == set(codes)
+    got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = fp8_excess(got, _oracle(inp))
+    _report(f"every gate code d={d}", err)
+    assert np.all(np.isfinite(got))
     assert err <= TOL["fp8"]
 
 
