@@ -121,6 +121,26 @@ def test_eps_values(eps):
     assert err <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("qk_scale,g_scale", [(2.0 ** -10, 1.0), (32.0, 32.0)], ids=["qk_near_eps", "large"])
+def test_scaled_inputs(dtype, qk_scale, g_scale):
+    """q and k scaled by powers of two (exact in bf16) so that mean(q^2) comes
+    down to eps (2^-10: ~1e-6) or far above it, and gates scaled into the
+    sigmoid's saturated range (x32): the folded q-side normalisation, whose eps
+    term moves into the denominator, and the gate at the ends of their range."""
+    from workloads import f32_to_bf16_bits
+    inp = make_inputs(5, 9, 13, 2, 128, dtype, seed=43)
+    for name, sc in (("q", qk_scale), ("k", qk_scale), ("g", g_scale)):
+        inp[name] = (inp[name] * np.float32(sc)).astype(np.float32)
+        if dtype == "bf16":
+            inp[name + "_bits"] = f32_to_bf16_bits(inp[name])
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"scaled q,k x{qk_scale:g} g x{g_scale:g} {dtype}", err, TOL[dtype])
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[dtype]
+
+
 def test_degenerate_rows():
     """All-negative q rows give exactly zero output; zero k rows add nothing."""
     inp = make_inputs(2, 5, 9, 2, 128, "bf16", seed=9)
