@@ -114,6 +114,21 @@ def test_token_causal_chained_calls(dtype, include_self):
     assert rel_err(z.astype(np.float64), rz) <= Z_TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("qk_scale,g_scale", [(2.0 ** -10, 1.0), (32.0, 32.0)], ids=["qk_near_eps", "large"])
+def test_token_causal_scaled_inputs(dtype, qk_scale, g_scale):
+    """q and k scaled by powers of two (exact in bf16) down to where mean(q^2)
+    meets eps, or up with the gates in the sigmoid's saturated range: the
+    walk's folded normalisation (eps * rms(q) in the denominator) and gate."""
+    from workloads import f32_to_bf16_bits
+    inp = make_inputs(3, 6, 8, 2, 128, dtype, seed=44)
+    for name, sc in (("q", qk_scale), ("k", qk_scale), ("g", g_scale)):
+        inp[name] = (inp[name] * np.float32(sc)).astype(np.float32)
+        if dtype == "bf16":
+            inp[name + "_bits"] = f32_to_bf16_bits(inp[name])
+    _check(f"tc scaled q,k x{qk_scale:g} g x{g_scale:g} {dtype}", inp, True)
+
+
 def test_token_causal_first_token_strict_is_zero():
     """Strictly earlier tokens and no carried state: token 0 reads nothing and
     its output is exactly zero."""
