@@ -26,8 +26,16 @@ constexpr int kDefaultTargetWg1 = 512;
 constexpr int kDefaultTargetWgAcc1 = 256;
 constexpr int kDefaultTargetWg2 = 2048;
 // The paired-head output kernel (bf16, d = 128) runs two workgroups per CU
-// (720p/60s in the full step: 722 us at 1024, 740 us at 3072).
-constexpr int kDefaultTargetWgPair2 = 1024;
+// (kPair2Slots at once).  Its launch is sized in whole rounds: one round, with
+// chunks of at least kPair2MinTiles tiles (each workgroup first reads its two
+// heads' 128 KB of state), or two rounds when one round's chunks would exceed
+// kPair2LongChunk tokens.  Measured in the full step: 720p/60s 680 us at two
+// rounds (1024 workgroups); 720p/5s with 32 heads 78 us at 512 workgroups
+// against 91 us at 592; 480p 23 us with 192-token chunks against 30 us with
+// 64-token ones.
+constexpr int kPair2Slots = 512;
+constexpr int kPair2MinTiles = 3;
+constexpr int kPair2LongChunk = 2048;
 
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
@@ -88,7 +96,11 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
 
   G.pass1_reg = (narrow && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
   const int target1 = G.pass1_reg ? kDefaultTargetWgAcc1 : kDefaultTargetWg1;
-  const int want1 = ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
+  // the register-accumulating kernel runs one workgroup per CU: rounding the
+  // chunk count down keeps the launch to one round of workgroups (20 heads:
+  // 240 workgroups, not 256 and then 4 more)
+  const int want1 = G.pass1_reg ? env_int("GLA_PASS1_WORKGROUPS", target1) / per_seg_heads
+                                : ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
@@ -106,8 +118,14 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && env_int("GLA_PASS2_GENERIC", 0) != 1)
                      ? 2 : 0;
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
-  const int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", G.pass2_pair ? kDefaultTargetWgPair2 : kDefaultTargetWg2),
-                             per_seg_units2);
+  int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", kDefaultTargetWg2), per_seg_units2);
+  if (G.pass2_pair && env_int("GLA_PASS2_WORKGROUPS", 0) == 0) {
+    want2 = kPair2Slots / per_seg_units2;   // chunks per segment in one round
+    if (want2 < 1) want2 = 1;
+    if ((long)ceil_div(tiles_per_seg, want2) * kTile > kPair2LongChunk) want2 = 2 * kPair2Slots / per_seg_units2;
+    const int most = ceil_div(tiles_per_seg, kPair2MinTiles);
+    if (want2 > most) want2 = most;
+  }
   int cps2 = want2 < 1 ? 1 : want2;
   if (cps2 > tiles_per_seg) cps2 = tiles_per_seg;
   while (!rope_fits((long)ceil_div(tiles_per_seg, cps2) * kTile) && cps2 < tiles_per_seg) ++cps2;
