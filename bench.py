@@ -323,6 +323,9 @@ def main(argv=None):
                     help="operator form: the workload's own (bidirectional or block-causal), or the token-level "
                          "causal form with the own token included (token-causal) or excluded (-strict)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="independent sequences per call ([B, N, heads, d] tensors, items drawn with seeds "
+                         "seed, seed + 1, ...); tokens/s and bytes count all items")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -370,7 +373,12 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     w = WORKLOADS[args.workload]
-    profiled = args.dtype is None or args.dtype == w.dtype   # profiles/ hold the default-dtype kernels
+    B = args.batch
+    if B < 1:
+        print("--batch must be at least 1", file=sys.stderr)
+        return 2
+    # profiles/ hold the default-dtype, single-sequence kernels
+    profiled = (args.dtype is None or args.dtype == w.dtype) and B == 1
     if args.dtype is not None:
         import dataclasses
         w = dataclasses.replace(w, dtype=args.dtype)
@@ -378,18 +386,25 @@ def main(argv=None):
     log(f"[bench] workload {w.name}: grid {w.T}x{w.H}x{w.W} N={w.N} heads={w.heads} d={w.d} {w.dtype}")
     t0 = time.time()
     inp = make_workload_inputs(w, seed=args.seed, keep_f32=(w.dtype == "f32"))
-    log(f"[bench] inputs drawn in {time.time() - t0:.1f} s")
+    items = [inp] + [make_workload_inputs(w, seed=args.seed + b, keep_f32=(w.dtype == "f32")) for b in range(1, B)]
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f} s" + (f" ({B} items)" if B > 1 else ""))
+
+    def upload_one(it, name):
+        if w.dtype == "bf16":
+            return torch.from_numpy(it[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        if w.dtype == "fp8":
+            return torch.from_numpy(it[name + "_bits"]).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(it[name]).to(dev)
 
     def upload(name):
-        if w.dtype == "bf16":
-            return torch.from_numpy(inp[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-        if w.dtype == "fp8":
-            return torch.from_numpy(inp[name + "_bits"]).to(dev).view(torch.float8_e4m3fn)
-        return torch.from_numpy(inp[name]).to(dev)
+        if B == 1:
+            return upload_one(inp, name)
+        return torch.stack([upload_one(it, name) for it in items]).contiguous()
 
     # Working sets that would sit in the 256 MB Infinity Cache are rotated over
     # enough copies (> 1 GB total) that each step reads from HBM.
-    sets = max(1, -(-1_000_000_000 // w.alg_bytes())) if w.alg_bytes() < 1_000_000_000 else 1
+    call_bytes = B * w.alg_bytes()
+    sets = max(1, -(-1_000_000_000 // call_bytes)) if call_bytes < 1_000_000_000 else 1
     bufs = []
     for i in range(sets):
         t = {n: upload(n) for n in ("q", "k", "v", "g", "beta")}
@@ -398,8 +413,9 @@ def main(argv=None):
     rms_w = torch.from_numpy(inp["rms_w"]).to(dev)
     causal = token_causal or w.block_frames is not None
     # carried state of the causal forms: each step continues the previous one's
-    state_S = torch.zeros((w.heads, w.d, w.d), dtype=torch.float32, device=dev) if causal else None
-    state_z = torch.zeros((w.heads, w.d), dtype=torch.float32, device=dev) if causal else None
+    lead = () if B == 1 else (B,)
+    state_S = torch.zeros(lead + (w.heads, w.d, w.d), dtype=torch.float32, device=dev) if causal else None
+    state_z = torch.zeros(lead + (w.heads, w.d), dtype=torch.float32, device=dev) if causal else None
     torch.cuda.synchronize()
     log(f"[bench] {sets} input set(s) resident on {torch.cuda.get_device_name(dev)}; form {args.form}")
 
@@ -431,13 +447,13 @@ def main(argv=None):
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
     ms_step = elapsed * 1e3 / args.steps
-    tokens_s = w.N / (ms_step * 1e-3)
-    alg_step = w.alg_bytes() + (2 * w.heads * (w.d * w.d + w.d) * 4 if token_causal else 0)
+    tokens_s = B * w.N / (ms_step * 1e-3)
+    alg_step = B * (w.alg_bytes() + (2 * w.heads * (w.d * w.d + w.d) * 4 if token_causal else 0))
     step_gbps = alg_step / (ms_step * 1e-3) / 1e9
     kernels = {k: {"ms_per_launch": (ms / n if n else None), "launches": n} for k, (ms, n) in kt.items()}
     dom = max(("state_partial_kernel", "output_kernel"), key=lambda k: kt[k][0])
     dom_ms = kt[dom][0] / max(1, kt[dom][1])
-    achieved = kernel_alg_bytes(w, dom, token_causal) / (dom_ms * 1e-3) / 1e9
+    achieved = B * kernel_alg_bytes(w, dom, token_causal) / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(dom, label, token_causal) if profiled else None
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
@@ -474,7 +490,7 @@ def main(argv=None):
         "config": {
             "workload": w.name,
             "grid": f"{w.T}x{w.H}x{w.W}",
-            "tokens": w.N,
+            "tokens": B * w.N,
             "heads": w.heads,
             "head_dim": w.d,
             "eps": w.eps,
@@ -482,6 +498,7 @@ def main(argv=None):
                      [args.form] if token_causal else
                      "bidirectional" if w.block_frames is None else f"block-causal F={w.block_frames}"),
             "input_sets": sets,
+            "batch": B,
         },
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
@@ -497,10 +514,11 @@ def main(argv=None):
             "traffic": traffic,
         },
         "mfma": {k: {
-            "achieved": kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12,
+            "achieved": B * kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12,
             "peak": MFMA_PEAK_TFLOPS[w.dtype],
             "unit": "TFLOP/s",
-            "frac": kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+            "frac": B * kernel_alg_flops(w, k, token_causal) / (kt[k][0] / kt[k][1] * 1e-3) / 1e12
+            / MFMA_PEAK_TFLOPS[w.dtype],
         } for k in ("state_partial_kernel", "output_kernel") if kt[k][1]},
         "cpu_baseline": cpu,
     }

@@ -13,6 +13,9 @@ PyTorch provides device memory and streams.
 
 q, k, v, g: [N, heads, d] (float32, bfloat16 or float8_e4m3fn, contiguous, on the GPU),
 beta: [N, heads] same dtype, rms_w: [d] float32, N = T*H*W, d in {32, 64, 128}.
+A leading batch dimension ([B, N, heads, d], beta [B, N, heads], states
+[B, heads, d, d] and [B, heads, d]) runs B independent sequences of the same
+grid in one call.
 """
 from __future__ import annotations
 
@@ -85,18 +88,23 @@ def _check(name, t, shape, dtype, device):
 
 
 def _common(q, k, v, beta, g, rms_w, grid, out):
+    """Checks the tensors; returns (batch or None, T, H, W, heads, d, dtype code, out)."""
     torch = _torch()
-    if q.dim() != 3:
-        raise ValueError("q must be [N, heads, d]")
+    if q.dim() not in (3, 4):
+        raise ValueError("q must be [N, heads, d] or [B, N, heads, d]")
     T, H, W = (int(x) for x in grid)
-    N, heads, d = (int(x) for x in q.shape)
+    batch = int(q.shape[0]) if q.dim() == 4 else None
+    N, heads, d = (int(x) for x in q.shape[-3:])
     if N != T * H * W:
         raise ValueError(f"q has {N} tokens but the grid {T}x{H}x{W} has {T * H * W}")
+    if batch is not None and batch < 1:
+        raise ValueError("the batch dimension must be at least 1")
     if q.device.type != "cuda":
         raise ValueError("tensors must be on the GPU")
     dt = q.dtype
     code = _dtype_code(q)
-    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("g", g, q.shape), ("beta", beta, (N, heads)),
+    bshape = tuple(q.shape[:-1])
+    for name, t, shp in (("k", k, q.shape), ("v", v, q.shape), ("g", g, q.shape), ("beta", beta, bshape),
                          ("q", q, q.shape)):
         _check(name, t, shp, dt, q.device)
     _check("rms_w", rms_w, (d,), torch.float32, q.device)
@@ -104,7 +112,14 @@ def _common(q, k, v, beta, g, rms_w, grid, out):
         out = torch.empty_like(q)
     else:
         _check("out", out, q.shape, dt, q.device)
-    return T, H, W, heads, d, code, out
+    return batch, T, H, W, heads, d, code, out
+
+
+def _check_state(state_S, state_z, batch, heads, d, device):
+    torch = _torch()
+    lead = () if batch is None else (batch,)
+    _check("state_S", state_S, lead + (heads, d, d), torch.float32, device)
+    _check("state_z", state_z, lead + (heads, d), torch.float32, device)
 
 
 def _stream_handle(stream, device):
@@ -119,11 +134,15 @@ def _ptr(t):
 
 def forward(q, k, v, beta, g, rms_w, grid, eps: float = 1e-6, out=None, stream=None):
     """Bidirectional operator; returns ``out`` (allocated if not given)."""
-    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
-    st = load().gla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W, heads, d,
-                            float(eps), _ptr(out), _stream_handle(stream, q.device), code)
+    batch, T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w))
+    tail = (T, H, W, heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device), code)
+    if batch is None:
+        st, where = load().gla_forward(*args, *tail), "gla_forward"
+    else:
+        st, where = load().gla_forward_batch(*args, batch, *tail), "gla_forward_batch"
     if st != 0:
-        raise GlaError(st, "gla_forward")
+        raise GlaError(st, where)
     return out
 
 
@@ -134,15 +153,17 @@ def block_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, block_
     state after the last block.  ``t_offset`` is the absolute frame of the
     call's first frame (a multiple of ``block_frames``) when a long video is
     streamed through successive calls.  Returns ``out``."""
-    torch = _torch()
-    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
-    _check("state_S", state_S, (heads, d, d), torch.float32, q.device)
-    _check("state_z", state_z, (heads, d), torch.float32, q.device)
-    st = load().gla_block_causal_forward_at(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
-                                            heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
-                                            _ptr(state_S), _ptr(state_z), int(block_frames), int(t_offset), code)
+    batch, T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    _check_state(state_S, state_z, batch, heads, d, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w))
+    tail = (T, H, W, heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device), _ptr(state_S),
+            _ptr(state_z), int(block_frames), int(t_offset), code)
+    if batch is None:
+        st, where = load().gla_block_causal_forward_at(*args, *tail), "gla_block_causal_forward_at"
+    else:
+        st, where = load().gla_block_causal_forward_batch(*args, batch, *tail), "gla_block_causal_forward_batch"
     if st != 0:
-        raise GlaError(st, "gla_block_causal_forward_at")
+        raise GlaError(st, where)
     return out
 
 
@@ -154,16 +175,17 @@ def token_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, includ
     state after the last token.  ``t_offset`` is the absolute frame of the
     call's first frame when a sequence is streamed through successive calls.
     Returns ``out``."""
-    torch = _torch()
-    T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
-    _check("state_S", state_S, (heads, d, d), torch.float32, q.device)
-    _check("state_z", state_z, (heads, d), torch.float32, q.device)
-    st = load().gla_token_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W,
-                                         heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device),
-                                         _ptr(state_S), _ptr(state_z), 1 if include_self else 0, int(t_offset),
-                                         code)
+    batch, T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    _check_state(state_S, state_z, batch, heads, d, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w))
+    tail = (T, H, W, heads, d, float(eps), _ptr(out), _stream_handle(stream, q.device), _ptr(state_S),
+            _ptr(state_z), 1 if include_self else 0, int(t_offset), code)
+    if batch is None:
+        st, where = load().gla_token_causal_forward(*args, *tail), "gla_token_causal_forward"
+    else:
+        st, where = load().gla_token_causal_forward_batch(*args, batch, *tail), "gla_token_causal_forward_batch"
     if st != 0:
-        raise GlaError(st, "gla_token_causal_forward")
+        raise GlaError(st, where)
     return out
 
 

@@ -55,14 +55,15 @@ enum class Form { bidirectional, block_causal, token_causal };
 
 // Segment length: the whole sequence, one block of latent frames, or (token-
 // causal form) a multiple of the 32-token tile chosen for parallelism.
-int segment_length(Form form, int T, int H, int W, int heads, int block_frames) {
+// (Per batch item: segments never straddle items.)
+int segment_length(Form form, int T, int H, int W, int heads, int block_frames, int batch) {
   const long N = (long)T * H * W;
   if (form == Form::block_causal) {
     const int frames = (block_frames > 0 && block_frames < T) ? block_frames : T;
     return frames * H * W;
   }
   if (form == Form::token_causal) {
-    const int want = ceil_div(env_int("GLA_TOKEN_CAUSAL_WORKGROUPS", kDefaultTargetWgTokenCausal), heads);
+    const int want = ceil_div(env_int("GLA_TOKEN_CAUSAL_WORKGROUPS", kDefaultTargetWgTokenCausal), (long)heads * batch);
     const int nseg = want < 1 ? 1 : want;
     const long len = ((N + nseg - 1) / nseg + kTokenTile - 1) / kTokenTile * kTokenTile;
     return (int)(len < kTokenTile ? kTokenTile : len);
@@ -73,12 +74,17 @@ int segment_length(Form form, int T, int H, int W, int heads, int block_frames) 
 // narrow: the I/O dtype is bf16 or fp8, whose rows the fast d = 128 pass-1 kernel takes as bf16
 // words; bf16_io: the I/O dtype is bf16
 Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, bool token_causal, bool narrow,
-              bool bf16_io) {
+              bool bf16_io, int batch) {
   Geometry G{};
-  G.T = T; G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
-  G.N = T * H * W;
+  G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
+  G.batch = batch;
+  G.T_item = T;
+  G.n_item = T * H * W;
+  G.T = batch * T;
+  G.N = batch * G.n_item;
   G.seg_len = seg_len;
-  G.nseg = ceil_div(G.N, G.seg_len);
+  G.segs_item = ceil_div(G.n_item, G.seg_len);
+  G.nseg = batch * G.segs_item;
   G.token_causal = token_causal ? 1 : 0;
   G.states_exclusive = token_causal ? 1 : 0;
   const int tiles_per_seg = ceil_div(G.seg_len, kTile);
@@ -223,13 +229,14 @@ Range range_of(const void* p, size_t bytes) {
 
 int validate(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
              int T, int H, int W, int heads, int d, float eps, const void* out, int dtype, bool causal,
-             const float* S, const float* z, int block_frames) {
+             const float* S, const float* z, int block_frames, int batch) {
   if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16 && dtype != GLA_DTYPE_FP8_E4M3) return GLA_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return GLA_ERR_UNSUPPORTED_D;
-  if (T < 0 || H < 0 || W < 0 || heads < 1) return GLA_ERR_SHAPE;
+  if (T < 0 || H < 0 || W < 0 || heads < 1 || batch < 1) return GLA_ERR_SHAPE;
   if (!(std::isfinite(eps) && eps >= FLT_MIN)) return GLA_ERR_SHAPE;
   if (causal && block_frames < 1) return GLA_ERR_SHAPE;
-  const long long N = (long long)T * H * W;
+  if ((long long)batch * T >= (1LL << 31)) return GLA_ERR_SHAPE;
+  const long long N = (long long)batch * T * H * W;   // tokens of all items
   if (N >= (1LL << 31)) return GLA_ERR_SHAPE;
   if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
   if (heads > (1 << 20)) return GLA_ERR_SHAPE;
@@ -251,8 +258,8 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   for (const Range& r : rin)
     if (overlap(rout, r)) return GLA_ERR_ALIAS;
   if (causal) {
-    const Range rs = range_of(S, (size_t)heads * d * d * 4);
-    const Range rz = range_of(z, (size_t)heads * d * 4);
+    const Range rs = range_of(S, (size_t)batch * heads * d * d * 4);
+    const Range rz = range_of(z, (size_t)batch * heads * d * 4);
     if (overlap(rs, rz) || overlap(rs, rout) || overlap(rz, rout)) return GLA_ERR_ALIAS;
     for (const Range& r : rin)
       if (overlap(rs, r) || overlap(rz, r)) return GLA_ERR_ALIAS;
@@ -261,21 +268,22 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
 }
 
 int run(Form form, const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
-        int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S, float* z,
-        int block_frames, int t_offset, int include_self) {
+        int batch, int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S,
+        float* z, int block_frames, int t_offset, int include_self) {
   const bool causal = form != Form::bidirectional;
   const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z,
-                          form == Form::block_causal ? block_frames : 1);
+                          form == Form::block_causal ? block_frames : 1, batch);
   if (st != GLA_OK) return st;
-  const long long N = (long long)T * H * W;
+  const long long N = (long long)batch * T * H * W;
   if (N == 0) return GLA_OK;
 
-  const int seg_len = segment_length(form, T, H, W, heads, block_frames);
+  const int seg_len = segment_length(form, T, H, W, heads, block_frames, batch);
   Geometry G = plan(T, H, W, heads, d, eps, seg_len, form == Form::token_causal,
-                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16);
+                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16, batch);
   G.t_offset = t_offset;
   G.include_self = include_self;
-  const size_t rope_bytes = align256(((size_t)T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
+  const size_t rope_bytes =
+      align256(((size_t)G.T * (d / 8) + (size_t)H * (3 * d / 16) + (size_t)W * (3 * d / 16)) * 8);
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
   const size_t state_bytes = align256((size_t)G.nseg * heads * sz * 4);
@@ -323,39 +331,63 @@ const char* const kKernelNames[gla::kNumKernels] = {"rope_table_kernel", "state_
 
 extern "C" {
 
+int gla_forward_batch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                      const float* rms_w, int batch, int T, int H, int W, int heads, int d, float eps, void* out,
+                      void* stream, int dtype) {
+  return run(Form::bidirectional, q, k, v, beta, g, rms_w, batch, T, H, W, heads, d, eps, out, stream, dtype, nullptr,
+             nullptr, 0, 0, 0);
+}
+
 int gla_forward(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
                 int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype) {
-  return run(Form::bidirectional, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, nullptr,
-             nullptr, 0, 0, 0);
+  return gla_forward_batch(q, k, v, beta, g, rms_w, 1, T, H, W, heads, d, eps, out, stream, dtype);
+}
+
+int gla_block_causal_forward_batch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                                   const float* rms_w, int batch, int T, int H, int W, int heads, int d, float eps,
+                                   void* out, void* stream, float* state_S, float* state_z, int block_frames,
+                                   int t_offset, int dtype) {
+  const bool frames_ok = block_frames >= 1 && t_offset >= 0 && t_offset % block_frames == 0 &&
+                         (long long)t_offset + T <= INT32_MAX;
+  if (!frames_ok) {
+    // validate the rest first so dtype/d errors keep their precedence
+    const int st =
+        validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1, batch);
+    return st != GLA_OK ? st : GLA_ERR_SHAPE;
+  }
+  return run(Form::block_causal, q, k, v, beta, g, rms_w, batch, T, H, W, heads, d, eps, out, stream, dtype, state_S,
+             state_z, block_frames, t_offset, 0);
 }
 
 int gla_block_causal_forward_at(const void* q, const void* k, const void* v, const void* beta, const void* g,
                                 const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
                                 void* stream, float* state_S, float* state_z, int block_frames, int t_offset,
                                 int dtype) {
-  const bool frames_ok = block_frames >= 1 && t_offset >= 0 && t_offset % block_frames == 0 &&
-                         (long long)t_offset + T <= INT32_MAX;
-  if (!frames_ok) {
+  return gla_block_causal_forward_batch(q, k, v, beta, g, rms_w, 1, T, H, W, heads, d, eps, out, stream, state_S,
+                                        state_z, block_frames, t_offset, dtype);
+}
+
+int gla_token_causal_forward_batch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                                   const float* rms_w, int batch, int T, int H, int W, int heads, int d, float eps,
+                                   void* out, void* stream, float* state_S, float* state_z, int include_self,
+                                   int t_offset, int dtype) {
+  const bool args_ok = (include_self == 0 || include_self == 1) && t_offset >= 0 && (long long)t_offset + T <= INT32_MAX;
+  if (!args_ok) {
     // validate the rest first so dtype/d errors keep their precedence
-    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
+    const int st =
+        validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1, batch);
     return st != GLA_OK ? st : GLA_ERR_SHAPE;
   }
-  return run(Form::block_causal, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S,
-             state_z, block_frames, t_offset, 0);
+  return run(Form::token_causal, q, k, v, beta, g, rms_w, batch, T, H, W, heads, d, eps, out, stream, dtype, state_S,
+             state_z, 0, t_offset, include_self);
 }
 
 int gla_token_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
                              const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
                              void* stream, float* state_S, float* state_z, int include_self, int t_offset,
                              int dtype) {
-  const bool args_ok = (include_self == 0 || include_self == 1) && t_offset >= 0 && (long long)t_offset + T <= INT32_MAX;
-  if (!args_ok) {
-    // validate the rest first so dtype/d errors keep their precedence
-    const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, true, state_S, state_z, 1);
-    return st != GLA_OK ? st : GLA_ERR_SHAPE;
-  }
-  return run(Form::token_causal, q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, state_S,
-             state_z, 0, t_offset, include_self);
+  return gla_token_causal_forward_batch(q, k, v, beta, g, rms_w, 1, T, H, W, heads, d, eps, out, stream, state_S,
+                                        state_z, include_self, t_offset, dtype);
 }
 
 int gla_block_causal_forward(const void* q, const void* k, const void* v, const void* beta, const void* g,
@@ -380,7 +412,7 @@ const char* gla_status_string(int status) {
   }
 }
 
-int gla_version(void) { return (1 << 16) | 3; }
+int gla_version(void) { return (1 << 16) | 4; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

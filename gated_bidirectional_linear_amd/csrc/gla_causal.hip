@@ -233,8 +233,8 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   const int units = G.heads / HP;
   const int seg = lin / units;
   const int head0 = (lin - seg * units) * HP;
-  const long seg_begin = (long)seg * G.seg_len;
-  const long seg_end = min(seg_begin + (long)G.seg_len, (long)G.N);
+  long seg_begin, seg_end;
+  seg_bounds(G, seg, seg_begin, seg_end);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -18,6 +18,15 @@ struct Chunk {
 // consecutive heads, so (after the XCD swizzle) all heads of a token range run
 // on one XCD at the same time: their rows share DRAM pages and the beta rows
 // (one cache line holds every head of a token) are fetched into one L2.
+// Token range [s0, s1) of segment `seg`: within its batch item, whose last
+// segment may be shorter.
+__device__ __forceinline__ void seg_bounds(const Geometry& G, int seg, long& s0, long& s1) {
+  const int item = seg / G.segs_item;
+  const long base = (long)item * G.n_item;
+  s0 = base + (long)(seg - item * G.segs_item) * G.seg_len;
+  s1 = min(s0 + (long)G.seg_len, base + (long)G.n_item);
+}
+
 __device__ __forceinline__ Chunk chunk_of(int lin, const Geometry& G, int cps, int chunk_len) {
   Chunk c;
   const int ci = lin / G.heads;          // chunk index within a head, over all segments
@@ -25,8 +34,8 @@ __device__ __forceinline__ Chunk chunk_of(int lin, const Geometry& G, int cps, i
   c.seg = ci / cps;
   c.index = ci;
   const int j = ci - c.seg * cps;
-  const long s0 = (long)c.seg * G.seg_len;
-  const long s1 = min(s0 + (long)G.seg_len, (long)G.N);
+  long s0, s1;
+  seg_bounds(G, c.seg, s0, s1);
   c.begin = min(s0 + (long)j * chunk_len, s1);
   c.end = min(c.begin + (long)chunk_len, s1);
   return c;

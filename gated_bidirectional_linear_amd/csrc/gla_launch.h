@@ -37,13 +37,19 @@ constexpr int kRopeLdsEntriesCausal = 1792;
 
 // Token partition shared by all kernels of one call.  A segment is the unit of
 // causality: the whole sequence (bidirectional) or one block of latent frames.
+// A batch of independent sequences lies one item after another along the token
+// axis; segments never straddle items.
 struct Geometry {
-  int T, H, W;
-  int N;        // T*H*W
+  int T, H, W;  // T: frames of all items (batch * T_item), the RoPE table's frame rows
+  int N;        // tokens of all items: batch * n_item
   int heads;
   int d;
-  int seg_len;  // tokens per segment (the last one may be shorter)
-  int nseg;
+  int batch;     // items
+  int T_item;    // frames per item (RoPE positions restart at every item)
+  int n_item;    // tokens per item, T_item * H * W
+  int seg_len;   // tokens per segment (the last one of an item may be shorter)
+  int segs_item; // segments per item
+  int nseg;      // batch * segs_item
   int cps1;     // pass-1 chunks per segment (<= kMaxChunks)
   int chunk1;   // pass-1 tokens per chunk (multiple of the 64-token tile)
   int cps2;     // pass-2 chunks per segment

@@ -337,8 +337,8 @@ __global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_wave
   const int ci = lin / npairs;
   const int pair = lin - ci * npairs;
   const int seg = ci / G.cps2;
-  const long s0 = (long)seg * G.seg_len;
-  const long s1 = min(s0 + (long)G.seg_len, (long)G.N);
+  long s0, s1;
+  seg_bounds(G, seg, s0, s1);
   const long cbeg = min(s0 + (long)(ci - seg * G.cps2) * G.chunk2, s1);
   const long cend = min(cbeg + (long)G.chunk2, s1);
   const int h0 = HP * pair;

@@ -8,9 +8,11 @@ namespace gla {
 // 1. RoPE tables
 // ===========================================================================
 template <int D>
-// Frame t of the call sits at absolute frame t_offset + t (streaming across
-// calls); rows and columns always start at 0.
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W, int t_offset) {
+// Frame row t (of all T frames of the batch) holds item frame t % T_item, at
+// absolute frame t_offset + t % T_item (streaming across calls); rows and
+// columns always start at 0.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W, int t_offset,
+                                                         int T_item) {
   using R = Rope<D>;
   const long total = (long)T * R::PT + (long)H * R::PY + (long)W * R::PX;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -18,7 +20,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
   long pos, i;
   int da;
   if (idx < (long)T * R::PT) {
-    pos = idx / R::PT + t_offset; i = idx % R::PT; da = D / 4;
+    pos = (idx / R::PT) % T_item + t_offset; i = idx % R::PT; da = D / 4;
   } else if (idx < (long)T * R::PT + (long)H * R::PY) {
     const long r = idx - (long)T * R::PT;
     pos = r / R::PY; i = r % R::PY; da = 3 * D / 8;
@@ -32,9 +34,10 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 
 // ===========================================================================
 // 3. Reduce chunk partials per segment (pairwise tree of fixed shape), then
-//    prefix over segments on top of the carried state: inclusive of the
-//    segment (bidirectional and block-causal forms) or exclusive (the
-//    token-causal form, whose segments are walked token by token).
+//    prefix over the segments of a batch item on top of its carried state:
+//    inclusive of the segment (bidirectional and block-causal forms) or
+//    exclusive (the token-causal form, whose segments are walked token by
+//    token).  One thread per (state element, head, item).
 // ===========================================================================
 template <int D>
 __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restrict__ partial,
@@ -44,22 +47,25 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
   constexpr int SZ = D * D + D;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
+  const int b = blockIdx.z;   // batch item
   if (e >= SZ) return;
+  const size_t hb = (size_t)b * G.heads + h;   // (item, head) of the carried state
   float running = 0.f;
-  if (S_in != nullptr) running = (e < D * D) ? S_in[(size_t)h * D * D + e] : z_in[(size_t)h * D + (e - D * D)];
-  const float* src = partial + (size_t)h * G.nseg * G.cps1 * SZ + e;
+  if (S_in != nullptr) running = (e < D * D) ? S_in[hb * D * D + e] : z_in[hb * D + (e - D * D)];
+  const int sfirst = b * G.segs_item;   // this item's first segment
+  const float* src = partial + ((size_t)h * G.nseg + sfirst) * G.cps1 * SZ + e;
   if (G.cps1 == 1) {
     // one partial per segment: the tree is the partial itself; the loads of
     // 8 segments are issued together
     constexpr int kBatch = 8;
-    for (int s0 = 0; s0 < G.nseg; s0 += kBatch) {
+    for (int s0 = 0; s0 < G.segs_item; s0 += kBatch) {
       float x[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) x[i] = (s0 + i < G.nseg) ? src[(size_t)(s0 + i) * SZ] : 0.f;
+      for (int i = 0; i < kBatch; ++i) x[i] = (s0 + i < G.segs_item) ? src[(size_t)(s0 + i) * SZ] : 0.f;
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        if (s0 + i >= G.nseg) break;
-        float* dst = states + ((size_t)(s0 + i) * G.heads + h) * SZ + e;
+        if (s0 + i >= G.segs_item) break;
+        float* dst = states + ((size_t)(sfirst + s0 + i) * G.heads + h) * SZ + e;
         if (G.states_exclusive) *dst = running;
         running += x[i];
         if (!G.states_exclusive) *dst = running;
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
     // (exactly), so they are skipped: the same sums in the same order
     int P = 1;
     while (P < G.cps1) P <<= 1;
-    for (int s = 0; s < G.nseg; ++s) {
+    for (int s = 0; s < G.segs_item; ++s) {
       float v[kMaxChunks];
 #pragma unroll
       for (int i = 0; i < kMaxChunks; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
@@ -80,14 +86,15 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
 #pragma unroll
         for (int i = 0; i < w; ++i) v[i] += v[i + w];
       }
-      if (G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
+      float* dst = states + ((size_t)(sfirst + s) * G.heads + h) * SZ + e;
+      if (G.states_exclusive) *dst = running;
       running += v[0];
-      if (!G.states_exclusive) states[((size_t)s * G.heads + h) * SZ + e] = running;
+      if (!G.states_exclusive) *dst = running;
     }
   }
   if (S_out != nullptr) {
-    if (e < D * D) S_out[(size_t)h * D * D + e] = running;
-    else z_out[(size_t)h * D + (e - D * D)] = running;
+    if (e < D * D) S_out[hb * D * D + e] = running;
+    else z_out[hb * D + (e - D * D)] = running;
   }
 }
 
@@ -96,7 +103,8 @@ hipError_t launch_rope_table(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   const long total = (long)G.T * (D / 8) + (long)G.H * (3 * D / 16) + (long)G.W * (3 * D / 16);
   const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL((rope_table_kernel<D>), dim3(blocks), dim3(256), 0, a.stream, a.rope, G.T, G.H, G.W, G.t_offset);
+  hipLaunchKernelGGL((rope_table_kernel<D>), dim3(blocks), dim3(256), 0, a.stream, a.rope, G.T, G.H, G.W, G.t_offset,
+                     G.T_item);
   return hipGetLastError();
 }
 
@@ -104,7 +112,7 @@ template <int D>
 hipError_t launch_state_reduce(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   constexpr int SZ = D * D + D;
-  dim3 grid((SZ + 255) / 256, G.heads);
+  dim3 grid((SZ + 255) / 256, G.heads, G.batch);
   hipLaunchKernelGGL((state_reduce_kernel<D>), grid, dim3(256), 0, a.stream, (const float*)a.partial, a.S_in, a.z_in,
                      a.states, a.S_out, a.z_out, G);
   return hipGetLastError();

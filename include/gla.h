@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   GLA_OK = 0,
   GLA_ERR_NULL = -1,          /* a required pointer is NULL */
-  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, block_frames < 1, bad t_offset or include_self,
+  GLA_ERR_SHAPE = -2,         /* T, H, W < 0, heads < 1, batch < 1, block_frames < 1, bad t_offset or include_self,
                                  eps not finite or below FLT_MIN, size overflow (N >= 2^31,
                                  N*heads*d >= 2^40, or a token row heads*d*elem_size >= 2^26 bytes) */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
@@ -170,6 +170,38 @@ int gla_token_causal_forward(const void* q, const void* k, const void* v, const 
                              const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
                              void* stream, float* state_S, float* state_z, int include_self, int t_offset,
                              int dtype);
+
+/*
+ * Batches of independent sequences (the streaming design's constant-memory
+ * state carried per video, SANA-Video notes, key design 2, for several videos
+ * at once), in one launch sequence.  Each of `batch` items is a sequence of
+ * the same (T, H, W) grid with its own state; the items do not interact.
+ *
+ *   q, k, v, g, out : [batch, N, heads, d] (item b's rows follow item b-1's)
+ *   beta            : [batch, N, heads]
+ *   state_S, state_z: [batch, heads, d, d] and [batch, heads, d] float32 (the
+ *                     causal forms): item b's carried state, read on entry and
+ *                     overwritten with the item's state after the call
+ *   batch           : >= 1; batch * T < 2^31 and batch * N * heads * d < 2^40
+ *                     (GLA_ERR_SHAPE otherwise)
+ * Every other argument is the single-sequence call's and applies to every
+ * item alike (t_offset included: all items are at the same frames of their
+ * videos).  Item b's output and state equal the single-sequence call on item
+ * b's tensors; the kernels cover all items at once, which fills the GPU where
+ * one short item would not.  The single-sequence calls are these with
+ * batch = 1.
+ */
+int gla_forward_batch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                      const float* rms_w, int batch, int T, int H, int W, int heads, int d, float eps,
+                      void* out, void* stream, int dtype);
+int gla_block_causal_forward_batch(const void* q, const void* k, const void* v, const void* beta,
+                                   const void* g, const float* rms_w, int batch, int T, int H, int W,
+                                   int heads, int d, float eps, void* out, void* stream, float* state_S,
+                                   float* state_z, int block_frames, int t_offset, int dtype);
+int gla_token_causal_forward_batch(const void* q, const void* k, const void* v, const void* beta,
+                                   const void* g, const float* rms_w, int batch, int T, int H, int W,
+                                   int heads, int d, float eps, void* out, void* stream, float* state_S,
+                                   float* state_z, int include_self, int t_offset, int dtype);
 
 /* Static text for a gla_status value (never NULL). */
 const char* gla_status_string(int status);

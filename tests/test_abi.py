@@ -39,7 +39,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
-    assert lib.gla_version() & 0xFFFF >= 3   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal
+    assert lib.gla_version() & 0xFFFF >= 4   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal;
+    #                                          1.4: batches
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
@@ -184,3 +185,45 @@ def test_binding_checks_shapes_before_the_device():
     q = torch.zeros(31, 2, 32)
     with pytest.raises(ValueError):
         gla.forward(q, q, q, torch.zeros(31, 2), q, torch.ones(32), (2, 4, 4))
+
+
+def fb(lib, batch=2, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_forward_batch(p[0], p[1], p[2], p[3], p[4], p[5], batch, T, H, W, heads, d, eps, p[6], None, dtype)
+
+
+def bcb(lib, batch=2, F=1, t_offset=0, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_block_causal_forward_batch(p[0], p[1], p[2], p[3], p[4], p[5], batch, T, H, W, heads, d, eps,
+                                              p[6], None, p[7], p[8], F, t_offset, dtype)
+
+
+def tcb(lib, batch=2, include_self=1, t_offset=0, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_token_causal_forward_batch(p[0], p[1], p[2], p[3], p[4], p[5], batch, T, H, W, heads, d, eps,
+                                              p[6], None, p[7], p[8], include_self, t_offset, dtype)
+
+
+def test_batch_argument_errors(lib):
+    for call in (fb, bcb, tcb):
+        assert call(lib, batch=0) == E_SHAPE
+        assert call(lib, batch=-3) == E_SHAPE
+        assert call(lib, batch=0, dtype=7) == E_DTYPE                  # dtype keeps its precedence
+        assert call(lib, batch=1 << 20, T=1 << 11, H=1, W=1) == E_SHAPE  # batch * T frames past 2^31
+        assert call(lib, batch=1 << 10, T=1 << 10, H=32, W=32, heads=8, d=128) == E_SHAPE   # past 2^40 elements
+        assert call(lib, batch=3, T=0, ptrs=[None] * 10) == OK           # empty grid
+    assert bcb(lib, F=3, t_offset=4) == E_SHAPE
+    assert tcb(lib, include_self=2) == E_SHAPE
+
+
+def test_batch_extents_in_alias_checks(lib):
+    """The tensors of all items count: a second item's rows or state overlap."""
+    item_rows = 2 * 4 * 4 * 2 * 32 * 2           # one item's q bytes (bf16)
+    p = list(P)
+    p[6] = ctypes.c_void_p(A + item_rows)        # out right after item 0 of q
+    assert fb(lib, batch=2, ptrs=p) == E_ALIAS
+    item_state = 2 * 32 * 32 * 4                  # one item's state_S bytes
+    p = list(P)
+    p[8] = ctypes.c_void_p(A + 7 * (1 << 36) + item_state)   # state_z right after item 0 of state_S
+    assert bcb(lib, batch=2, ptrs=p) == E_ALIAS
+    assert tcb(lib, batch=2, ptrs=p) == E_ALIAS
