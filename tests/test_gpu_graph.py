@@ -70,3 +70,27 @@ def test_token_causal_graph_replay():
                                  S, z, include_self=True, eps=inp["eps"], out=out)
     _graph_replays(call, out, ref)
     assert torch.equal(S, S_ref) and torch.equal(z, z_ref)
+
+
+def test_batched_token_causal_graph_replay():
+    """A batched call ([B, N, heads, d], per-item states) under capture."""
+    torch = pytest.importorskip("torch")
+    import gated_bidirectional_linear_amd as gla
+    B, heads, d = 3, 2, 128
+    items = [to_device(make_inputs(2, 6, 7, heads, d, "bf16", seed=53 + b)) for b in range(B)]
+    dev = {n: torch.stack([it[n] for it in items]).contiguous() for n in ("q", "k", "v", "g", "beta")}
+    rms_w = items[0]["rms_w"]
+    S = torch.zeros((B, heads, d, d), dtype=torch.float32, device="cuda")
+    z = torch.zeros((B, heads, d), dtype=torch.float32, device="cuda")
+    ref = gla.token_causal_forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], rms_w, (2, 6, 7), S, z)
+    torch.cuda.synchronize()
+    S_ref, z_ref = S.clone(), z.clone()
+    out = torch.empty_like(ref)
+
+    def call():
+        S.zero_()
+        z.zero_()
+        gla.token_causal_forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], rms_w, (2, 6, 7), S, z,
+                                 out=out)
+    _graph_replays(call, out, ref)
+    assert torch.equal(S, S_ref) and torch.equal(z, z_ref)
