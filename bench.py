@@ -246,28 +246,63 @@ def write_stats_summary(stats_csv: str, workload: str, commands: str, token_caus
     print(f"wrote {path}")
 
 
+def host_threads():
+    """(usable cores, BLAS description) of this process: the cores in its CPU
+    affinity mask, and each BLAS library numpy loaded with its thread count."""
+    cores = len(os.sched_getaffinity(0))
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas.append({"library": i.get("internal_api"), "version": i.get("version"),
+                             "threads": i.get("num_threads")})
+    except Exception:
+        pass
+    return cores, blas
+
+
+def timed_oracle(fn):
+    """Run fn() with the BLAS threads set to every usable core; returns
+    (seconds, cores, blas description)."""
+    cores, _ = host_threads()
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        limit = None
+    try:
+        _, blas = host_threads()
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return dt, cores, blas
+
+
 def cpu_baseline(w, inp, heads_sample: int):
     """Time the fp64 oracle on `heads_sample` heads of the full workload (all
     tokens, complete state and output) and scale to the whole workload."""
-    import numpy as np
     import oracle.gla_oracle as orc
     from workloads import head_slice_f32
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     heads = list(range(min(heads_sample, w.heads)))
     sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
         **inp, **{n: inp[n][:, heads] for n in ("q", "k", "v", "g", "beta")}}
-    t0 = time.perf_counter()
-    orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"], sub["eps"])
-    dt = time.perf_counter() - t0
+    if w.block_frames is not None:
+        run = lambda: orc.gla_block_causal_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"],  # noqa: E731
+                                                   sub["rms_w"], sub["grid"], sub["eps"], w.block_frames)
+    else:
+        run = lambda: orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"],  # noqa: E731
+                                      sub["grid"], sub["eps"])
+    dt, cores, blas = timed_oracle(run)
     per_call = dt * w.heads / len(heads)
     return {
         "value": w.N / per_call,
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": cores,
+        "blas": blas,
         "kind": "oracle",
         "sample": f"{len(heads)} of {w.heads} heads at full N={w.N} (whole state and output), "
                   f"{dt:.2f} s, scaled x{w.heads / len(heads):g} to the full workload",
@@ -281,11 +316,6 @@ def cpu_baseline_token_causal(w, inp, include_self: bool, heads_sample: int = 2,
     import numpy as np
     import oracle.gla_oracle as orc
     from workloads import head_slice_f32
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     hw = w.H * w.W
     frames = max(1, min(w.T, round(target_tokens / hw)))
     n = frames * hw
@@ -293,15 +323,15 @@ def cpu_baseline_token_causal(w, inp, include_self: bool, heads_sample: int = 2,
     sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
         **inp, **{k: inp[k][:, heads] for k in ("q", "k", "v", "g", "beta")}}
     part = {k: sub[k][:n] for k in ("q", "k", "v", "g", "beta")}
-    t0 = time.perf_counter()
-    orc.gla_token_causal_rows(part["q"], part["k"], part["v"], part["beta"], part["g"], sub["rms_w"],
-                              (frames, w.H, w.W), w.eps, np.arange(n), include_self=include_self)
-    dt = time.perf_counter() - t0
+    dt, cores, blas = timed_oracle(
+        lambda: orc.gla_token_causal_rows(part["q"], part["k"], part["v"], part["beta"], part["g"], sub["rms_w"],
+                                          (frames, w.H, w.W), w.eps, np.arange(n), include_self=include_self))
     scale = (w.N / n) * w.heads / len(heads)
     return {
         "value": w.N / (dt * scale),
         "unit": "tokens/s",
-        "cores": int(threads),
+        "cores": cores,
+        "blas": blas,
         "kind": "oracle",
         "sample": f"token-causal running sums, {len(heads)} of {w.heads} heads, first {frames} of {w.T} frames "
                   f"({n} tokens, every row), {dt:.2f} s, scaled x{scale:.4g} to the full workload",
@@ -458,6 +488,22 @@ def main(argv=None):
     for k, v in kernels.items():
         log(f"[bench]   {k:22s} {v['ms_per_launch'] * 1e3 if v['ms_per_launch'] else 0:9.1f} us/launch")
 
+    warm = None
+    if sets > 1:
+        # the same steps on one input set, which the 256 MB Infinity Cache can
+        # hold between steps: the "warm" figure, reported next to the cold one
+        for i in range(3):
+            step(0)
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        for i in range(args.steps):
+            step(0)
+        torch.cuda.synchronize()
+        ms_w = (time.perf_counter() - t_w) * 1e3 / args.steps
+        warm = {"ms_per_step": ms_w, "tokens_per_s": B * w.N / (ms_w * 1e-3),
+                "hbm_gbps": alg_step / (ms_w * 1e-3) / 1e9, "input_sets": 1}
+        log(f"[bench] warm (one input set): {ms_w * 1e3:.1f} us/step")
+
     if args.calib_copy_mib > 0:
         # an elementwise streaming kernel of known size: read and write calib MiB
         src = torch.ones((args.calib_copy_mib << 20) // 4, dtype=torch.float32, device=dev)
@@ -500,6 +546,8 @@ def main(argv=None):
             "input_sets": sets,
             "batch": B,
         },
+        "cache": "cold (inputs rotated over sets larger than the 256 MB Infinity Cache)" if sets > 1 else "cold",
+        "warm": warm,
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "alg_bytes_per_step": alg_step,

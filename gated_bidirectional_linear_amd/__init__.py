@@ -35,6 +35,9 @@ __all__ = [
     "SIGNATURES",
     "timing_enable",
     "timing_read",
+    "plan_override",
+    "plan_reset",
+    "PLAN_KNOBS",
     "DTYPE_F32",
     "DTYPE_BF16",
     "DTYPE_FP8_E4M3",
@@ -187,6 +190,31 @@ def token_causal_forward(q, k, v, beta, g, rms_w, grid, state_S, state_z, includ
     if st != 0:
         raise GlaError(st, where)
     return out
+
+
+# Launch-plan knobs of include/gla_internal.h (tests and tuning sweeps only).
+PLAN_KNOBS = {
+    "pass1_generic": 0,
+    "pass1_workgroups": 1,
+    "pass2_generic": 2,
+    "pass2_workgroups": 3,
+    "rope_global": 4,
+    "token_causal_workgroups": 5,
+}
+
+
+def plan_override(knob: str, value: int) -> None:
+    """Set a launch-plan knob (0 = default).  Process-wide; for tests and
+    tuning sweeps only: every plan computes the same operator."""
+    st = load().gla_plan_override(PLAN_KNOBS[knob], int(value))
+    if st != 0:
+        raise GlaError(st, "gla_plan_override")
+
+
+def plan_reset() -> None:
+    """Restore the default launch plan for every knob."""
+    for knob in PLAN_KNOBS:
+        plan_override(knob, 0)
 
 
 def timing_enable(on: bool = True) -> None:

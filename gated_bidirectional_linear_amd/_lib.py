@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgla.so")
 
 # Exported symbols and their ctypes signatures, in the order include/gla.h
-# declares them.
+# and then include/gla_internal.h declare them.
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
@@ -34,6 +34,7 @@ SIGNATURES = {
     "gla_timing_enable": (_i, [_i]),
     "gla_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), _i]),
     "gla_kernel_name": (ctypes.c_char_p, [_i]),
+    "gla_plan_override": (_i, [_i, _i]),
 }
 
 _LIB = None

@@ -5,11 +5,12 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
 #include "../../include/gla.h"
+#include "../../include/gla_internal.h"
 #include "gla_launch.h"
 
 namespace {
@@ -19,7 +20,8 @@ using gla::Geometry;
 constexpr int kTile = 64;
 // Workgroups aimed for per launch: pass 1 writes one partial state per
 // workgroup, so it stays near two per CU (256 CUs); pass 2 has no such cost
-// and takes more for load balance.  Overridable for tuning sweeps.
+// and takes more for load balance.  gla_plan_override changes them for tests
+// and tuning sweeps.
 constexpr int kDefaultTargetWg1 = 512;
 // The bf16, d = 128 pass-1 kernel keeps whole states in registers and runs
 // one workgroup per CU.
@@ -37,12 +39,22 @@ constexpr int kPair2Slots = 512;
 constexpr int kPair2MinTiles = 3;
 constexpr int kPair2LongChunk = 2048;
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (s == nullptr || *s == 0) return dflt;
-  const long v = std::strtol(s, nullptr, 10);
-  return (v >= 1 && v <= (1 << 24)) ? (int)v : dflt;
-}
+// Launch-plan overrides (include/gla_internal.h): process-wide, 0 = the
+// measured default.  Every call reads them once, into a Knobs snapshot, so a
+// concurrent gla_plan_override cannot change a plan halfway through.
+std::atomic<int> g_knobs[GLA_PLAN_NUM_KNOBS];
+
+struct Knobs {
+  int v[GLA_PLAN_NUM_KNOBS];
+  static Knobs snapshot() {
+    Knobs k;
+    for (int i = 0; i < GLA_PLAN_NUM_KNOBS; ++i) k.v[i] = g_knobs[i].load(std::memory_order_relaxed);
+    return k;
+  }
+  // the knob's value, or dflt where it is unset
+  int get(int knob, int dflt) const { return v[knob] > 0 ? v[knob] : dflt; }
+  bool on(int knob) const { return v[knob] > 0; }
+};
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -56,14 +68,14 @@ enum class Form { bidirectional, block_causal, token_causal };
 // Segment length: the whole sequence, one block of latent frames, or (token-
 // causal form) a multiple of the 32-token tile chosen for parallelism.
 // (Per batch item: segments never straddle items.)
-int segment_length(Form form, int T, int H, int W, int heads, int block_frames, int batch) {
+int segment_length(Form form, int T, int H, int W, int heads, int block_frames, int batch, const Knobs& kn) {
   const long N = (long)T * H * W;
   if (form == Form::block_causal) {
     const int frames = (block_frames > 0 && block_frames < T) ? block_frames : T;
     return frames * H * W;
   }
   if (form == Form::token_causal) {
-    const int want = ceil_div(env_int("GLA_TOKEN_CAUSAL_WORKGROUPS", kDefaultTargetWgTokenCausal), (long)heads * batch);
+    const int want = ceil_div(kn.get(GLA_PLAN_TOKEN_CAUSAL_WORKGROUPS, kDefaultTargetWgTokenCausal), (long)heads * batch);
     const int nseg = want < 1 ? 1 : want;
     const long len = ((N + nseg - 1) / nseg + kTokenTile - 1) / kTokenTile * kTokenTile;
     return (int)(len < kTokenTile ? kTokenTile : len);
@@ -74,7 +86,7 @@ int segment_length(Form form, int T, int H, int W, int heads, int block_frames, 
 // narrow: the I/O dtype is bf16 or fp8, whose rows the fast d = 128 pass-1 kernel takes as bf16
 // words; bf16_io: the I/O dtype is bf16
 Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, bool token_causal, bool narrow,
-              bool bf16_io, int batch) {
+              bool bf16_io, int batch, const Knobs& kn) {
   Geometry G{};
   G.H = H; G.W = W; G.heads = heads; G.d = d; G.eps = eps;
   G.batch = batch;
@@ -100,13 +112,13 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     return yx + frames * (d / 8) <= entries;
   };
 
-  G.pass1_reg = (narrow && d == 128 && env_int("GLA_PASS1_GENERIC", 0) != 1) ? 1 : 0;
+  G.pass1_reg = (narrow && d == 128 && !kn.on(GLA_PLAN_PASS1_GENERIC)) ? 1 : 0;
   const int target1 = G.pass1_reg ? kDefaultTargetWgAcc1 : kDefaultTargetWg1;
   // the register-accumulating kernel runs one workgroup per CU: rounding the
   // chunk count down keeps the launch to one round of workgroups (20 heads:
   // 240 workgroups, not 256 and then 4 more)
-  const int want1 = G.pass1_reg ? env_int("GLA_PASS1_WORKGROUPS", target1) / per_seg_heads
-                                : ceil_div(env_int("GLA_PASS1_WORKGROUPS", target1), per_seg_heads);
+  const int want1 = G.pass1_reg ? kn.get(GLA_PLAN_PASS1_WORKGROUPS, target1) / per_seg_heads
+                                : ceil_div(kn.get(GLA_PLAN_PASS1_WORKGROUPS, target1), per_seg_heads);
   int cps1 = want1 < 1 ? 1 : want1;
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
@@ -121,11 +133,10 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // instantiation spills registers at two workgroups per CU and measured slower than the
   // one-head kernel, so fp8 keeps the one-head kernel.
   // heads per workgroup of pass 2: pairs for bf16, d = 128 and an even head count
-  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && env_int("GLA_PASS2_GENERIC", 0) != 1)
-                     ? 2 : 0;
+  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && !kn.on(GLA_PLAN_PASS2_GENERIC)) ? 2 : 0;
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
-  int want2 = ceil_div(env_int("GLA_PASS2_WORKGROUPS", kDefaultTargetWg2), per_seg_units2);
-  if (G.pass2_pair && env_int("GLA_PASS2_WORKGROUPS", 0) == 0) {
+  int want2 = ceil_div(kn.get(GLA_PLAN_PASS2_WORKGROUPS, kDefaultTargetWg2), per_seg_units2);
+  if (G.pass2_pair && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
     want2 = kPair2Slots / per_seg_units2;   // chunks per segment in one round
     if (want2 < 1) want2 = 1;
     if ((long)ceil_div(tiles_per_seg, want2) * kTile > kPair2LongChunk) want2 = 2 * kPair2Slots / per_seg_units2;
@@ -143,9 +154,9 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     G.chunk2 = G.seg_len;
     G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
     // head pairs (bf16 operands, d = 128, even head count): 512-byte row segments
-    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && env_int("GLA_PASS2_GENERIC", 0) != 1) ? 2 : 0;
+    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && !kn.on(GLA_PLAN_PASS2_GENERIC)) ? 2 : 0;
   }
-  if (env_int("GLA_ROPE_GLOBAL", 0) == 1) G.rope_lds1 = G.rope_lds2 = 0;
+  if (kn.on(GLA_PLAN_ROPE_GLOBAL)) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
   if (!G.rope_lds1) G.pass1_reg = 0;
   if (!G.rope_lds2 && !token_causal) G.pass2_pair = 0;
@@ -235,11 +246,16 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   if (T < 0 || H < 0 || W < 0 || heads < 1 || batch < 1) return GLA_ERR_SHAPE;
   if (!(std::isfinite(eps) && eps >= FLT_MIN)) return GLA_ERR_SHAPE;
   if (causal && block_frames < 1) return GLA_ERR_SHAPE;
-  if ((long long)batch * T >= (1LL << 31)) return GLA_ERR_SHAPE;
-  const long long N = (long long)batch * T * H * W;   // tokens of all items
+  // each product below stays under 2^62: every factor is < 2^31 and the
+  // running product is checked against 2^31 before the next factor
+  const long long BT = (long long)batch * T;
+  if (BT >= (1LL << 31)) return GLA_ERR_SHAPE;
+  const long long BTH = BT * H;
+  if (BTH >= (1LL << 31) && W > 0) return GLA_ERR_SHAPE;
+  const long long N = W > 0 ? BTH * W : 0;   // tokens of all items
   if (N >= (1LL << 31)) return GLA_ERR_SHAPE;
-  if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
   if (heads > (1 << 20)) return GLA_ERR_SHAPE;
+  if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
   // the kernels address up to 64 token rows of all heads through one 32-bit
   // buffer range: a token row (heads * d elements) must stay below 2^26 bytes
   const long long es_row = dtype == GLA_DTYPE_BF16 ? 2 : (dtype == GLA_DTYPE_FP8_E4M3 ? 1 : 4);
@@ -277,9 +293,10 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   const long long N = (long long)batch * T * H * W;
   if (N == 0) return GLA_OK;
 
-  const int seg_len = segment_length(form, T, H, W, heads, block_frames, batch);
+  const Knobs kn = Knobs::snapshot();
+  const int seg_len = segment_length(form, T, H, W, heads, block_frames, batch, kn);
   Geometry G = plan(T, H, W, heads, d, eps, seg_len, form == Form::token_causal,
-                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16, batch);
+                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16, batch, kn);
   G.t_offset = t_offset;
   G.include_self = include_self;
   const size_t rope_bytes =
@@ -287,11 +304,19 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
   const size_t state_bytes = align256((size_t)G.nseg * heads * sz * 4);
+  const size_t scratch_bytes = rope_bytes + part_bytes + state_bytes;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  prepare_pool();
+  // no usable device (none present, or the runtime failed to start): report
+  // it before any allocation or launch
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return GLA_ERR_HIP;
+  }
   void* scratch = nullptr;
-  if (hipMallocAsync(&scratch, rope_bytes + part_bytes + state_bytes, hs) != hipSuccess || scratch == nullptr) {
+  prepare_pool();
+  if (hipMallocAsync(&scratch, scratch_bytes, hs) != hipSuccess || scratch == nullptr) {
     (void)hipGetLastError();
     return GLA_ERR_ALLOC;
   }
@@ -441,6 +466,12 @@ int gla_timing_read(double* ms, long long* launches, int n) {
   }
   tm.recs.clear();
   return st;
+}
+
+int gla_plan_override(int knob, int value) {
+  if (knob < 0 || knob >= GLA_PLAN_NUM_KNOBS || value < 0 || value > (1 << 24)) return GLA_ERR_SHAPE;
+  g_knobs[knob].store(value, std::memory_order_relaxed);
+  return GLA_OK;
 }
 
 const char* gla_kernel_name(int kernel_id) {

@@ -623,12 +623,12 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
       for (int rb = 0; rb < 4; ++rb)
         *reinterpret_cast<f32x4*>(row + 8 * rb) = (f32x4){n[4 * rb], n[4 * rb + 1], n[4 * rb + 2], n[4 * rb + 3]};
     }
-    float rden[TPT];
+    float den[TPT];
     if (rows) {
       if constexpr (C::MD) {
 #pragma unroll
         for (int i = 0; i < TPT; ++i)
-          rden[i] = __builtin_amdgcn_rcpf(dpz[i] + dins(hl)[tg * TPT + i] + G.eps * rq_scale[i]);
+          den[i] = dpz[i] + dins(hl)[tg * TPT + i] + G.eps * rq_scale[i];
         // running key sums after this tile
         const f32x4 za = *reinterpret_cast<const f32x4*>(zsum(hl) + 8 * cg);
         const f32x4 zb = *reinterpret_cast<const f32x4*>(zsum(hl) + 8 * cg + 4);
@@ -643,7 +643,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
           float dp = phq[i][0] * za.x + phq[i][1] * za.y + phq[i][2] * za.z + phq[i][3] * za.w +
                      phq[i][4] * zb.x + phq[i][5] * zb.y + phq[i][6] * zb.z + phq[i][7] * zb.w;
           dp = group_sum<C::CG>(dp);
-          rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * rq_scale[i]);
+          den[i] = dp + G.eps * rq_scale[i];
         }
       }
     }
@@ -665,8 +665,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
           ss += y[c] * y[c];
         }
         ss = group_sum<C::CG>(ss);
-        const float rd = rden[i];
-        const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
+        const float scale = out_scale(ss * (1.0f / D), den[i], G.eps);
 #pragma unroll
         for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
         BR::store(ors, voff[i], 0, Elem<E>::pack(y));

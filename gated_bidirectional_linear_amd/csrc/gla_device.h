@@ -396,6 +396,16 @@ __device__ __forceinline__ uint32_t relu2(uint32_t u) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, u), (s16x2){0, 0}));
 }
 
+// Output RMSNorm scale of x = y / den for a row whose gated numerator y has
+// mean square ms and whose denominator is den > 0:
+//   x / sqrt(mean(x^2) + eps) = y / sqrt(ms + eps * den^2).
+// No 1/den is formed, so a zero row (y = 0, den as small as eps^1.5) cannot
+// turn into inf * 0.  The floor at FLT_MIN keeps the reciprocal square root
+// finite when ms + eps * den^2 underflows (then y = 0 and the result is 0).
+__device__ __forceinline__ float out_scale(float ms, float den, float eps) {
+  return __builtin_amdgcn_rsqf(fmaxf(ms + eps * den * den, 1.17549435e-38f));
+}
+
 // Position (t, y, x) of a token on the latent grid, advanced without division.
 struct GridPos {
   int t, y, x;

@@ -35,8 +35,8 @@ struct OutputCfg {
 //   sigmoid(g) * S R phi(q^) / (phi(q^) . z + eps)
 //     = sigmoid(g) * S R phi(q) / (phi(q) . z + eps * r).
 // The MFMA therefore takes the rotated raw features, and the output RMSNorm
-// of x = y / den (y = sigmoid(g) * num) uses the per-token scale
-//   rden * rsqrt(rden^2 * mean(y^2) + eps),  rden = 1 / den.
+// of x = y / den (y = sigmoid(g) * num, den > 0) is w * y times the per-token
+// scale 1 / sqrt(mean(y^2) + eps * den^2) (out_scale), which needs no 1 / den.
 template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void output_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
     }
     pos.advance(adt, ady, adx, G.H, G.W);
 
-    float rden[C::TPT];
+    float den[C::TPT];
 #pragma unroll
     for (int i = 0; i < C::TPT; ++i) {
       float ph[8];
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
       dp = group_sum<C::CG>(dp);
       const float ms = ss * (1.0f / D) + G.eps;
       const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
-      rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * r);   // v_rcp_f32, 1 ulp
+      den[i] = dp + G.eps * r;
       R::apply(ph, cs[i]);
       L* dst = rqs + (tg * C::TPT + i) * C::RQ_PITCH + 8 * cg;
       if constexpr (Elem<L>::is_bf16) {
@@ -248,8 +248,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
         }
       }
       ss = group_sum<C::CG>(ss);
-      const float rd = rden[i];
-      const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
+      const float scale = out_scale(ss * (1.0f / D), den[i], G.eps);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
       BR::store(ors, voff[i], 0, Elem<E>::pack(y));   // rows past the chunk are dropped
@@ -426,7 +425,7 @@ __global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_wave
   // chunk read as zero, their stores are dropped), so the compiler's waits
   // cover exactly the rows in use.
   auto tile = [&](Raw (&qt)[TPT], Raw (&gt)[TPT], long t0) {
-    float rden[TPT];
+    float den[TPT];
     GridPos pp = pos;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -452,7 +451,7 @@ __global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_wave
       dp = group_sum<16>(dp);
       const float ms = ss * (1.0f / D) + G.eps;
       const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
-      rden[i] = __builtin_amdgcn_rcpf(dp + G.eps * r);
+      den[i] = dp + G.eps * r;
       R::apply(ph, cs);
       *reinterpret_cast<u32x4*>(rqs + ((i * TPI + tg) * HP + hl) * RQ_PITCH + 8 * c16) = Elem<bf16_t>::pack(ph);
     }
@@ -497,8 +496,7 @@ __global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_wave
         ss += y[c] * y[c];
       }
       ss = group_sum<16>(ss);
-      const float rd = rden[i];
-      const float scale = rd * __builtin_amdgcn_rsqf(rd * rd * (ss * (1.0f / D)) + G.eps);
+      const float scale = out_scale(ss * (1.0f / D), den[i], G.eps);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
       IO::store(ors, voff[i], y);   // rows past the chunk are dropped

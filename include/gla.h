@@ -26,7 +26,9 @@
  *   - 3D RoPE: channels [0,d/4) follow t, [d/4,5d/8) follow y, [5d/8,d)
  *     follow x; pair i of an axis slice is channels (2i,2i+1) and turns by
  *     pos * 10000^(-2i/d_axis), (u,w) -> (u cos a - w sin a, u sin a + w cos a);
- *     positions count from 0 in every call;
+ *     row and column positions count from 0; the frame position of frame t
+ *     of a call is t, plus t_offset in the calls that take one (streaming a
+ *     video through successive calls);
  *   - one eps for the q/k RMS normalisation, the denominator and the output
  *     RMSNorm.
  *
@@ -64,7 +66,7 @@ typedef enum {
                                  N*heads*d >= 2^40, or a token row heads*d*elem_size >= 2^26 bytes) */
   GLA_ERR_DTYPE = -3,         /* dtype is not a gla_dtype value */
   GLA_ERR_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
-  GLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
+  GLA_ERR_HIP = -5,           /* no usable device, or a HIP runtime call or kernel launch failed */
   GLA_ERR_ALLOC = -6,         /* temporary device memory could not be obtained */
   GLA_ERR_UNSUPPORTED_D = -7, /* head dim not in {32, 64, 128} */
   GLA_ERR_ALIAS = -8          /* out or the state overlaps another tensor */
@@ -90,8 +92,9 @@ typedef enum {
  *   rms_w      : [d] float32, output RMSNorm weight          (read)
  *   out        : [N, heads, d] in `dtype`                    (written; must not alias an input)
  *   T, H, W    : latent grid (frames, rows, columns), each >= 0; N = 0 is a no-op
- *   heads      : >= 1;  d : 32, 64 or 128;  eps : finite, >= FLT_MIN (a normal float, so
- *                rsqrt(mean(x^2) + eps) stays finite for an all-zero row)
+ *   heads      : >= 1;  d : 32, 64 or 128;  eps : finite, >= FLT_MIN (a normal float); rows
+ *                with phi(q^) = 0 (all-zero or all-negative q) give an all-zero output
+ *                row for every such eps
  * When N == 0 the tensor pointers may be NULL.
  * Returns GLA_OK or a negative gla_status.
  */

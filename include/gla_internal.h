@@ -1,0 +1,50 @@
+/*
+ * gla_internal.h -- launch-plan overrides of libgla.so, for tests and tuning
+ * sweeps only.  Not part of the operator's interface (gla.h): a program that
+ * only computes the operator never needs it.
+ *
+ * Every call of the operator picks its kernels and launch sizes from the
+ * shapes alone, with defaults chosen by measurement.  The tests use these
+ * knobs to reach every kernel variant (the LDS-staged pass-1 kernel, the
+ * one-head output kernel, RoPE rows from the global table, other chunk
+ * counts) on shapes where the default plan would not.  The results of every
+ * variant are the operator's results; only speed differs.
+ *
+ * The knobs are process-wide (all threads and devices).  Each operator call
+ * reads all of them once when it starts, so a change affects calls that start
+ * after gla_plan_override returns.  The library reads no environment
+ * variable.
+ */
+#ifndef GLA_INTERNAL_H
+#define GLA_INTERNAL_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_PLAN_PASS1_GENERIC = 0,            /* > 0: LDS-staged pass-1 kernel instead of the register-
+                                            accumulating one (bf16 and fp8 at d = 128) */
+  GLA_PLAN_PASS1_WORKGROUPS = 1,         /* > 0: workgroups aimed for by pass 1 (chunks per segment
+                                            follow from it, at most 64) */
+  GLA_PLAN_PASS2_GENERIC = 2,            /* > 0: one head per workgroup in the output kernel and in the
+                                            token-causal walk */
+  GLA_PLAN_PASS2_WORKGROUPS = 3,         /* > 0: workgroups aimed for by the output kernel */
+  GLA_PLAN_ROPE_GLOBAL = 4,              /* > 0: RoPE rows read from the global table instead of LDS */
+  GLA_PLAN_TOKEN_CAUSAL_WORKGROUPS = 5,  /* > 0: (head, segment) units aimed for by the token-causal
+                                            walk (segment length follows from it) */
+  GLA_PLAN_NUM_KNOBS = 6
+} gla_plan_knob;
+
+/*
+ * Set knob `knob` to `value`; 0 restores the default plan for that knob.
+ * Returns GLA_OK, or GLA_ERR_SHAPE (nothing changed) for an unknown knob or a
+ * value outside [0, 2^24].
+ */
+int gla_plan_override(int knob, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_INTERNAL_H */

@@ -110,3 +110,37 @@ def run_token_causal(dev: dict, grid, eps, include_self=True, S0=None, z0=None, 
                                    S, z, include_self=include_self, eps=eps, t_offset=t_offset)
     torch.cuda.synchronize()
     return out, S, z
+
+
+def grouped_head_error(out, inp, ref_fn, kind="rel", rows=None, group=8, label=""):
+    """Error of a full-size GPU output over every head, against the oracle run
+    on `group` heads at a time (bounded host memory).
+
+    out    : GPU output [N, heads, d]
+    inp    : a bits-only bf16 or fp8 input set (make_inputs(..., keep_f32=False))
+    ref_fn : oracle call on an input set holding only the group's heads;
+             returns [len(rows) or N, group, d]
+    kind   : "rel" -> max|got - ref| / max|ref|; "fp8" -> fp8_excess's
+             numerator over max|ref|, both maxima taken over all heads
+    rows   : token rows compared (None: every row)
+    """
+    from workloads import head_slice_f32
+    torch = torch_mod()
+    heads = out.shape[1]
+    worst, top = 0.0, 0.0
+    idx = None if rows is None else torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(out.device)
+    for h0 in range(0, heads, group):
+        hs = list(range(h0, min(h0 + group, heads)))
+        ref = np.asarray(ref_fn(head_slice_f32(inp, hs)), np.float64)
+        sel = out[:, h0:h0 + len(hs), :] if idx is None else out[idx][:, h0:h0 + len(hs), :]
+        got = to_f64(sel)
+        if kind == "fp8":
+            ex = np.abs(got - ref) - 2.0 ** -4 * np.abs(ref) - 2.0 ** -10
+            worst = max(worst, float(np.max(ex)))
+        else:
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+        top = max(top, float(np.max(np.abs(ref))))
+        print(f"[parity] {label} heads {hs[0]}..{hs[-1]}: running error {max(worst, 0.0) / max(top, 1e-300):.3e}",
+              flush=True)
+        del ref, got
+    return max(worst, 0.0) / (top if top > 0 else 1.0)

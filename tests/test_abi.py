@@ -12,15 +12,18 @@ import gated_bidirectional_linear_amd as gla
 from gated_bidirectional_linear_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gla.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gla_\w+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(gla_\w+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -227,3 +230,62 @@ def test_batch_extents_in_alias_checks(lib):
     p[8] = ctypes.c_void_p(A + 7 * (1 << 36) + item_state)   # state_z right after item 0 of state_S
     assert bcb(lib, batch=2, ptrs=p) == E_ALIAS
     assert tcb(lib, batch=2, ptrs=p) == E_ALIAS
+
+
+def test_plan_override_argument_errors(lib):
+    assert lib.gla_plan_override(-1, 1) == E_SHAPE
+    assert lib.gla_plan_override(6, 1) == E_SHAPE        # past GLA_PLAN_NUM_KNOBS
+    assert lib.gla_plan_override(0, -1) == E_SHAPE
+    assert lib.gla_plan_override(0, (1 << 24) + 1) == E_SHAPE
+    for knob in range(6):
+        assert lib.gla_plan_override(knob, 0) == OK
+
+
+def test_plan_knobs_match_the_header():
+    text = open(os.path.join(ROOT, "include", "gla_internal.h")).read()
+    knobs = dict((name.lower(), int(v)) for name, v in re.findall(r"GLA_PLAN_(\w+)\s*=\s*(\d+)", text))
+    knobs.pop("num_knobs")
+    assert knobs == gla.PLAN_KNOBS
+
+
+def test_library_reads_no_environment():
+    """The launch plan is not taken from the environment: no getenv in the
+    library's sources."""
+    csrc = os.path.join(ROOT, "gated_bidirectional_linear_amd", "csrc")
+    for name in os.listdir(csrc):
+        assert "getenv" not in open(os.path.join(csrc, name)).read(), name
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+from gated_bidirectional_linear_amd import _lib
+lib = _lib.load()
+hip = ctypes.CDLL("libamdhip64.so.7")
+n = ctypes.c_int(0)
+if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+    sys.exit(77)        # a device is visible: these fake pointers must not reach it
+A = 1 << 40
+p = [ctypes.c_void_p(A + i * (1 << 36)) for i in range(10)]
+r = [lib.gla_forward(p[0], p[1], p[2], p[3], p[4], p[5], 2, 4, 4, 2, 32, 1e-6, p[6], None, 1),
+     lib.gla_block_causal_forward(p[0], p[1], p[2], p[3], p[4], p[5], 2, 4, 4, 2, 32, 1e-6, p[6], None,
+                                  p[7], p[8], 1, 1),
+     lib.gla_token_causal_forward(p[0], p[1], p[2], p[3], p[4], p[5], 2, 4, 4, 2, 32, 1e-6, p[6], None,
+                                  p[7], p[8], 1, 0, 1)]
+print(r)
+sys.exit(0 if r == [-5, -5, -5] else 1)
+"""
+
+
+def test_compute_call_without_a_device_returns_hip_error():
+    """A valid call in a process that sees no GPU returns GLA_ERR_HIP (no
+    crash, nothing enqueued).  Run in a child process, which exits early if a
+    device is visible there."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT.format(root=ROOT)], capture_output=True,
+                         text=True, timeout=120)
+    if res.returncode == 77:
+        pytest.skip("a GPU is visible: the no-device path cannot be exercised here")
+    assert res.returncode == 0, res.stdout + res.stderr
+

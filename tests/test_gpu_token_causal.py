@@ -12,7 +12,8 @@ import pytest
 
 import oracle.gla_oracle as orc
 from workloads import WORKLOADS, make_inputs, make_workload_inputs, make_state, head_slice_f32
-from tests.gpu_helpers import TOL, Z_TOL, to_device, to_f64, rel_err, fp8_excess, run_token_causal
+from tests.gpu_helpers import (TOL, Z_TOL, to_device, to_f64, rel_err, fp8_excess, run_token_causal,
+                               grouped_head_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,11 +68,11 @@ def test_token_causal_shapes(shape, include_self):
 
 @pytest.mark.parametrize("wg", ["1", "3", "64"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_token_causal_segment_counts(monkeypatch, wg, dtype):
+def test_token_causal_segment_counts(plan, wg, dtype):
     """One segment walked by one workgroup per head, a few segments of many
     tiles, or many one-tile segments: the same result."""
     T, H, W, heads, d = 5, 7, 9, 2, 128
-    monkeypatch.setenv("GLA_TOKEN_CAUSAL_WORKGROUPS", str(int(wg) * heads))
+    plan("token_causal_workgroups", int(wg) * heads)
     print(f"[case] token-causal segments={wg} {dtype}", flush=True)
     inp = make_inputs(T, H, W, heads, d, dtype, seed=32)
     _check(f"tc segments {wg} {dtype}", inp, True)
@@ -140,15 +141,15 @@ def test_token_causal_first_token_strict_is_zero():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_token_causal_one_head_kernel(monkeypatch, dtype):
+def test_token_causal_one_head_kernel(plan, dtype):
     """d = 128 with the head-pair kernel switched off: the one-head walk."""
-    monkeypatch.setenv("GLA_PASS2_GENERIC", "1")
+    plan("pass2_generic", 1)
     inp = make_inputs(4, 5, 9, 4, 128, dtype, seed=38)
     _check(f"tc one-head kernel {dtype}", inp, True)
 
 
-def test_token_causal_global_rope_table(monkeypatch):
-    monkeypatch.setenv("GLA_ROPE_GLOBAL", "1")
+def test_token_causal_global_rope_table(plan):
+    plan("rope_global", 1)
     inp = make_inputs(4, 6, 7, 2, 128, "bf16", seed=36)
     _check("tc global rope", inp, True)
 
@@ -176,36 +177,71 @@ def test_token_causal_empty_grid_leaves_state():
     assert bool((S == 1.5).all()) and bool((z == 0.5).all())
 
 
+@pytest.mark.parametrize("eps", [float(np.finfo(np.float32).tiny), float(np.float32(1e-14))],
+                         ids=["flt_min", "1e-14"])
+@pytest.mark.parametrize("kernel", ["head_pair", "f32"])
+@pytest.mark.parametrize("include_self", [True, False])
+def test_token_causal_tiny_eps_zero_rows(include_self, kernel, eps):
+    """The smallest eps the interface accepts (FLT_MIN) and 1e-14, with
+    all-zero and all-negative q rows (exactly zero output), and in the strict
+    reading token 0 on a fresh state (no earlier token: numerator 0,
+    denominator eps * rms(q)), also exactly zero; the head-pair walk (bf16,
+    d = 128) and the one-head walk (fp32)."""
+    from workloads import f32_to_bf16_bits
+    dtype = "f32" if kernel == "f32" else "bf16"
+    d = 64 if kernel == "f32" else 128
+    inp = make_inputs(4, 5, 9, 4, d, dtype, seed=45, eps=eps)
+    inp["q"][5::5] = 0.0
+    inp["q"][1::5] = -np.abs(inp["q"][1::5])
+    inp["q"][0] = np.abs(inp["q"][0])
+    if dtype == "bf16":
+        inp["q_bits"] = f32_to_bf16_bits(inp["q"])
+    o = _check(f"tc eps={eps:.3e} {kernel} incl={include_self}", inp, include_self)
+    assert np.all(o[5::5] == 0) and np.all(o[1::5] == 0)
+    if not include_self:
+        assert np.all(o[0] == 0)
+    else:
+        assert np.any(o[0] != 0)
+
+
 @pytest.mark.parametrize("include_self,dtype", [(True, "bf16"), (False, "bf16"), (True, "fp8")])
 def test_token_causal_long_sequence_sampled(include_self, dtype):
     """720p/60s (N = 159,280, 32 heads) at full size in the default launch
-    plan: the oracle evaluates 3 heads at sampled tokens (segment boundaries
-    included) by running sums, and the final state of those heads."""
+    plan: every head at the same 2,100 tokens (every segment boundary, the
+    first and last tokens and random ones) against the oracle's running sums,
+    8 heads per oracle call, and the final state of every head against the
+    bidirectional state."""
     torch = pytest.importorskip("torch")
     w = dataclasses.replace(WORKLOADS["720p_60s"], dtype=dtype)
     print(f"[case] token-causal {w.name} {dtype} N={w.N} heads={w.heads} include_self={include_self}", flush=True)
     inp = make_workload_inputs(w, seed=0, keep_f32=False)
     dev = to_device(inp)
     out, S, z = run_token_causal(dev, inp["grid"], inp["eps"], include_self)
-    o32 = out.float()
-    assert bool(torch.isfinite(o32).all())
+    del dev
+    assert bool(torch.isfinite(out.float()).all())
     # default plan: 512 workgroups -> 16 segments of 9,984 tokens per head
     seg = 9984
     bounds = [s * seg + dlt for s in range(1, 16) for dlt in (-1, 0, 1)]
     rng = np.random.default_rng(321)
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, w.N - 1], bounds, rng.integers(0, w.N, 200)]))
-    heads = [0, 13, 31]
-    sub = head_slice_f32(inp, heads)
-    ref = orc.gla_token_causal_rows(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"],
-                                    sub["eps"], rows, include_self=include_self)
-    got = to_f64(out[torch.from_numpy(rows).cuda()][:, heads, :])
-    err = _out_err(got, ref, dtype)
-    print(f"[parity] tc 720p_60s {dtype} sampled incl={include_self}: error {err:.3e}", flush=True)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, w.N - 1], bounds, rng.integers(0, w.N, 2060)]))
+    assert len(rows) >= 2048
+
+    def ref_rows(sub):
+        return orc.gla_token_causal_rows(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"],
+                                         sub["grid"], sub["eps"], rows, include_self=include_self)
+
+    err = grouped_head_error(out, inp, ref_rows, kind="fp8" if dtype == "fp8" else "rel", rows=rows,
+                             label=f"tc 720p_60s {dtype} incl={include_self}")
+    print(f"[parity] tc 720p_60s {dtype} all heads, {len(rows)} rows, incl={include_self}: error {err:.3e}",
+          flush=True)
     assert err <= TOL[dtype]
-    parts = orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"],
-                            sub["eps"], rows=np.array([0]), return_parts=True)
-    assert rel_err(to_f64(S[heads]), parts["S"]) <= S_TOL[dtype]
-    assert rel_err(to_f64(z[heads]), parts["z"]) <= Z_TOL[dtype]
+    for h0 in range(0, w.heads, 8):
+        hs = list(range(h0, h0 + 8))
+        sub = head_slice_f32(inp, hs)
+        parts = orc.gla_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"], sub["grid"],
+                                sub["eps"], rows=np.array([0]), return_parts=True)
+        assert rel_err(to_f64(S[hs]), parts["S"]) <= S_TOL[dtype]
+        assert rel_err(to_f64(z[hs]), parts["z"]) <= Z_TOL[dtype]
 
 
 @pytest.mark.parametrize("include_self", [True, False])
