@@ -25,6 +25,7 @@ from ._lib import LIB_PATH, LibraryNotBuilt, SIGNATURES, load
 
 __all__ = [
     "forward",
+    "forward_noalloc",
     "block_causal_forward",
     "token_causal_forward",
     "status_string",
@@ -146,6 +147,22 @@ def forward(q, k, v, beta, g, rms_w, grid, eps: float = 1e-6, out=None, stream=N
         st, where = load().gla_forward_batch(*args, batch, *tail), "gla_forward_batch"
     if st != 0:
         raise GlaError(st, where)
+    return out
+
+
+def forward_noalloc(q, k, v, beta, g, rms_w, grid, eps: float = 1e-6, out=None, stream=None):
+    """The bidirectional operator through gla_forward_noalloc: the library
+    allocates no device memory (its scratch is a static 64 MiB device array;
+    calls that overlap on one device race on it).  ``out`` must be given by
+    callers that cannot allocate; otherwise it is allocated here.  Returns
+    ``out``."""
+    batch, T, H, W, heads, d, code, out = _common(q, k, v, beta, g, rms_w, grid, out)
+    if batch is not None:
+        raise ValueError("forward_noalloc takes one sequence ([N, heads, d] tensors)")
+    st = load().gla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(rms_w), T, H, W, heads,
+                                    d, float(eps), _ptr(out), _stream_handle(stream, q.device), code)
+    if st != 0:
+        raise GlaError(st, "gla_forward_noalloc")
     return out
 
 

@@ -29,6 +29,7 @@ SIGNATURES = {
                                             _vp, _vp, _vp, _i, _i, _i]),
     "gla_token_causal_forward_batch": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp,
                                             _vp, _vp, _vp, _i, _i, _i]),
+    "gla_forward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _i]),
     "gla_status_string": (ctypes.c_char_p, [_i]),
     "gla_version": (_i, []),
     "gla_timing_enable": (_i, [_i]),

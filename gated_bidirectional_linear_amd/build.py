@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgla.so")
-SOURCES = ["gla_tables.hip", "gla_state.hip", "gla_output.hip", "gla_causal.hip", "gla_dispatch.cpp", "gla_abi.cpp"]
+SOURCES = ["gla_tables.hip", "gla_state.hip", "gla_output.hip", "gla_causal.hip", "gla_noalloc.hip", "gla_dispatch.cpp",
+           "gla_abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -283,9 +283,11 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   return GLA_OK;
 }
 
+// fixed: when given, the call's scratch is that buffer (the allocation-free
+// entry point) instead of a stream-ordered allocation.
 int run(Form form, const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
         int batch, int T, int H, int W, int heads, int d, float eps, void* out, void* stream, int dtype, float* S,
-        float* z, int block_frames, int t_offset, int include_self) {
+        float* z, int block_frames, int t_offset, int include_self, const gla::FixedScratch* fixed = nullptr) {
   const bool causal = form != Form::bidirectional;
   const int st = validate(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, dtype, causal, S, z,
                           form == Form::block_causal ? block_frames : 1, batch);
@@ -305,6 +307,7 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
   const size_t state_bytes = align256((size_t)G.nseg * heads * sz * 4);
   const size_t scratch_bytes = rope_bytes + part_bytes + state_bytes;
+  if (fixed != nullptr && scratch_bytes > fixed->bytes) return GLA_ERR_TOO_LARGE;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   // no usable device (none present, or the runtime failed to start): report
@@ -315,10 +318,15 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
     return GLA_ERR_HIP;
   }
   void* scratch = nullptr;
-  prepare_pool();
-  if (hipMallocAsync(&scratch, scratch_bytes, hs) != hipSuccess || scratch == nullptr) {
-    (void)hipGetLastError();
-    return GLA_ERR_ALLOC;
+  if (fixed != nullptr) {
+    scratch = fixed->device_ptr(dev);
+    if (scratch == nullptr) return GLA_ERR_HIP;
+  } else {
+    prepare_pool();
+    if (hipMallocAsync(&scratch, scratch_bytes, hs) != hipSuccess || scratch == nullptr) {
+      (void)hipGetLastError();
+      return GLA_ERR_ALLOC;
+    }
   }
   char* base = static_cast<char*>(scratch);
 
@@ -341,7 +349,7 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
     NullTimer nt;
     e = gla::launch_operator(a, nt);
   }
-  const hipError_t ef = hipFreeAsync(scratch, hs);
+  const hipError_t ef = fixed != nullptr ? hipSuccess : hipFreeAsync(scratch, hs);
   if (e != hipSuccess || ef != hipSuccess) {
     (void)hipGetLastError();
     return GLA_ERR_HIP;
@@ -353,6 +361,15 @@ const char* const kKernelNames[gla::kNumKernels] = {"rope_table_kernel", "state_
                                                      "state_reduce_kernel", "output_kernel"};
 
 }  // namespace
+
+namespace gla {
+int forward_fixed_scratch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                          const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                          void* stream, int dtype, const FixedScratch& fixed) {
+  return run(Form::bidirectional, q, k, v, beta, g, rms_w, 1, T, H, W, heads, d, eps, out, stream, dtype, nullptr,
+             nullptr, 0, 0, 0, &fixed);
+}
+}  // namespace gla
 
 extern "C" {
 
@@ -433,11 +450,12 @@ const char* gla_status_string(int status) {
     case GLA_ERR_ALLOC: return "temporary device memory could not be obtained";
     case GLA_ERR_UNSUPPORTED_D: return "head dim must be 32, 64 or 128";
     case GLA_ERR_ALIAS: return "output or state buffer overlaps another tensor";
+    case GLA_ERR_TOO_LARGE: return "the call needs more scratch than the allocation-free entry point's static buffer holds";
     default: return "unknown status";
   }
 }
 
-int gla_version(void) { return (1 << 16) | 4; }
+int gla_version(void) { return (1 << 16) | 5; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

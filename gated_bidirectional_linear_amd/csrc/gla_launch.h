@@ -27,6 +27,8 @@
 #pragma once
 #include <hip/hip_runtime_api.h>
 
+#include <cstddef>
+
 namespace gla {
 
 constexpr int kMaxChunks = 64;   // chunk partials per segment reduced by one tree
@@ -91,5 +93,19 @@ struct Timer {
 };
 
 hipError_t launch_operator(const LaunchArgs& a, Timer& tm);
+
+// A scratch buffer that the caller holds for the whole process (the
+// allocation-free entry point's static device array): its address on device
+// `dev` (nullptr if it cannot be had) and its size in bytes.
+struct FixedScratch {
+  void* (*device_ptr)(int dev);
+  size_t bytes;
+};
+
+// The bidirectional operator (gla_forward) with its scratch in `fixed`:
+// GLA_ERR_TOO_LARGE, before anything is enqueued, when the call needs more.
+int forward_fixed_scratch(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                          const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                          void* stream, int dtype, const FixedScratch& fixed);
 
 }  // namespace gla

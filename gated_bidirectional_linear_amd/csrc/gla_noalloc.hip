@@ -1,0 +1,49 @@
+// The allocation-free entry point: gla_forward with its scratch (RoPE table,
+// chunk partials, per-segment states) in a static device array instead of a
+// stream-ordered allocation.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/gla.h"
+#include "gla_launch.h"
+
+namespace {
+// 64 MiB: the 720p/60s workload (159,280 tokens, 32 heads, d = 128) needs
+// 19 MB; any bidirectional call with at most 256 heads at d = 128 and a few
+// hundred thousand frames' RoPE rows fits.  Every device the library runs on
+// holds one copy until the process ends.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}  // namespace
+
+// The device array.  In host code `scratch` names a host-side shadow, not
+// device memory: host code uses only the address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_mu;
+void* g_scratch_ptr[kMaxDevices];   // scratch's address on each device, looked up once per device
+
+// Called with device `dev` current (the call's device).
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int gla_forward_noalloc(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                                   const float* rms_w, int T, int H, int W, int heads, int d, float eps, void* out,
+                                   void* stream, int dtype) {
+  const gla::FixedScratch fixed{scratch_on, kScratchBytes};
+  return gla::forward_fixed_scratch(q, k, v, beta, g, rms_w, T, H, W, heads, d, eps, out, stream, dtype, fixed);
+}

@@ -69,7 +69,8 @@ typedef enum {
   GLA_ERR_HIP = -5,           /* no usable device, or a HIP runtime call or kernel launch failed */
   GLA_ERR_ALLOC = -6,         /* temporary device memory could not be obtained */
   GLA_ERR_UNSUPPORTED_D = -7, /* head dim not in {32, 64, 128} */
-  GLA_ERR_ALIAS = -8          /* out or the state overlaps another tensor */
+  GLA_ERR_ALIAS = -8,         /* out or the state overlaps another tensor */
+  GLA_ERR_TOO_LARGE = -9      /* gla_forward_noalloc: the call needs more scratch than its static buffer */
 } gla_status;
 
 typedef enum {
@@ -205,6 +206,33 @@ int gla_token_causal_forward_batch(const void* q, const void* k, const void* v, 
                                    const void* g, const float* rms_w, int batch, int T, int H, int W,
                                    int heads, int d, float eps, void* out, void* stream, float* state_S,
                                    float* state_z, int include_self, int t_offset, int dtype);
+
+/*
+ * gla_forward without any device-memory allocation, for callers that cannot
+ * allocate: code under HIP graph capture that must not record allocation
+ * nodes, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments, layout, ownership, results (bit for bit) and errors as
+ * gla_forward.  Its scratch (RoPE table, chunk partial states, per-segment
+ * states) lives in a static device array of 64 MiB that each device the
+ * library runs on holds until the process ends; the call makes no hipMalloc,
+ * hipMallocAsync or hipFree.
+ *
+ * Limit: a call needing more than 64 MiB of scratch returns GLA_ERR_TOO_LARGE
+ * before anything is enqueued.  The need is about
+ *     (T*d/8 + (H + W)*3d/16)*8 + (P + 1)*heads*(d*d + d)*4 bytes,
+ * with P <= 64 chunk partials per head (about max(1, 256/heads) at d = 128 in
+ * bf16 or fp8, max(1, 512/heads) otherwise): the 720p/60s workload
+ * (159,280 tokens, 32 heads, d = 128) needs 19 MB.
+ *
+ * Concurrency: every call on one device uses that device's one array.  Calls
+ * that can overlap on a device (on different streams, or from different
+ * threads without ordering) race on it and give undefined results; calls on
+ * one stream are ordered and safe.  Nothing in the array must start at zero:
+ * each call writes every part of it that it reads.
+ */
+int gla_forward_noalloc(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                        const float* rms_w, int T, int H, int W, int heads, int d, float eps,
+                        void* out, void* stream, int dtype);
 
 /* Static text for a gla_status value (never NULL). */
 const char* gla_status_string(int status);

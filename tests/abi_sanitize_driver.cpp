@@ -163,6 +163,19 @@ int main() {
   for (int k = 0; k < GLA_PLAN_NUM_KNOBS; ++k) EXPECT(gla_plan_override(k, 7), GLA_OK);
   for (int k = 0; k < GLA_PLAN_NUM_KNOBS; ++k) EXPECT(gla_plan_override(k, 0), GLA_OK);
 
+  // a fixed scratch buffer too small for the call: rejected before any device work
+  {
+    const gla::FixedScratch tiny{[](int) -> void* { return nullptr; }, 1024};
+    Args a;
+    EXPECT(gla::forward_fixed_scratch(a.p[0], a.p[1], a.p[2], a.p[3], a.p[4], (const float*)a.p[5], a.T, a.H, a.W,
+                                      a.heads, a.d, a.eps, a.p[6], nullptr, a.dtype, tiny),
+           GLA_ERR_TOO_LARGE);
+    a.dtype = 9;
+    EXPECT(gla::forward_fixed_scratch(a.p[0], a.p[1], a.p[2], a.p[3], a.p[4], (const float*)a.p[5], a.T, a.H, a.W,
+                                      a.heads, a.d, a.eps, a.p[6], nullptr, a.dtype, tiny),
+           GLA_ERR_DTYPE);
+  }
+
   // a valid call with no device: GLA_ERR_HIP, nothing launched
   int count = 0;
   const bool device = hipGetDeviceCount(&count) == hipSuccess && count > 0;

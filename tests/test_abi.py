@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
            if h.endswith(".h")]
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS, E_TOO_LARGE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 def declared_functions():
@@ -42,9 +42,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
-    assert lib.gla_version() & 0xFFFF >= 4   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal;
-    #                                          1.4: batches
-    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS):
+    assert lib.gla_version() & 0xFFFF >= 5   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal;
+    #                                          1.4: batches; 1.5: gla_forward_noalloc
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS, E_TOO_LARGE):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
     assert lib.gla_status_string(-99).decode() == "unknown status"
@@ -289,3 +289,24 @@ def test_compute_call_without_a_device_returns_hip_error():
         pytest.skip("a GPU is visible: the no-device path cannot be exercised here")
     assert res.returncode == 0, res.stdout + res.stderr
 
+
+def fna(lib, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
+    p = list(P if ptrs is None else ptrs)
+    return lib.gla_forward_noalloc(p[0], p[1], p[2], p[3], p[4], p[5], T, H, W, heads, d, eps, p[6], None, dtype)
+
+
+def test_noalloc_validation_and_size_limit(lib):
+    """gla_forward_noalloc validates like gla_forward and rejects, before any
+    device work, calls whose scratch exceeds its 64 MiB static buffer."""
+    assert fna(lib, dtype=3) == E_DTYPE
+    assert fna(lib, d=48) == E_D
+    assert fna(lib, heads=0) == E_SHAPE
+    assert fna(lib, ptrs=[None] + P[1:]) == E_NULL
+    p = list(P)
+    p[6] = p[0]
+    assert fna(lib, ptrs=p) == E_ALIAS
+    assert fna(lib, T=0, ptrs=[None] * 10) == OK
+    # RoPE rows of 600,000 frames: 600,000 * 16 pairs * 8 bytes = 77 MB
+    assert fna(lib, T=600_000, H=1, W=1, heads=1, d=128) == E_TOO_LARGE
+    # 1,024 heads at d = 128: at least 2 * 1,024 states of 66 KB
+    assert fna(lib, T=2, H=4, W=4, heads=1024, d=128) == E_TOO_LARGE

@@ -1,0 +1,78 @@
+"""GPU tests of gla_forward_noalloc (the entry point for callers that cannot
+allocate device memory): through the C ABI, its output equals gla_forward's
+bit for bit on consecutive calls that share its static scratch array, the
+second on a smaller input, and matches the oracle."""
+import numpy as np
+import pytest
+
+import oracle.gla_oracle as orc
+from workloads import WORKLOADS, make_inputs, make_workload_inputs
+from tests.gpu_helpers import TOL, rel_err, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(dev, inp):
+    import torch
+    import gated_bidirectional_linear_amd as gla
+    ref = gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"], eps=inp["eps"])
+    out = torch.full_like(ref, float("nan"))
+    gla.forward_noalloc(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"],
+                        eps=inp["eps"], out=out)
+    torch.cuda.synchronize()
+    return ref, out
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_noalloc_equals_forward_on_consecutive_calls():
+    """720p/5s with 32 heads, then the smaller 480p grid, then the tiny fp32
+    grid: each noalloc call reuses the array the previous one wrote, and each
+    output equals gla_forward's bit for bit and the oracle within tolerance."""
+    import torch
+    cases = [WORKLOADS["720p_5s_h32"], WORKLOADS["480p"], WORKLOADS["tiny_f32"]]
+    for w in cases:
+        print(f"[case] noalloc {w.name} N={w.N} heads={w.heads} {w.dtype}", flush=True)
+        inp = make_workload_inputs(w, seed=0)
+        dev = to_device(inp)
+        ref, out = _both(dev, inp)
+        assert torch.equal(_bits(out), _bits(ref)), w.name
+        if w.N * w.heads <= 4290 * 20:
+            err = rel_err(to_f64(out), orc.gla_forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"],
+                                                       inp["rms_w"], inp["grid"], inp["eps"]))
+            print(f"[parity] noalloc {w.name}: rel err {err:.3e}", flush=True)
+            assert err <= TOL[w.dtype]
+
+
+def test_noalloc_ragged_shapes_and_repeat():
+    """Ragged grids on both output-kernel variants (odd and even head counts),
+    each called twice in a row: identical results every time."""
+    import torch
+    for shape in [(5, 9, 13, 3, 128), (3, 5, 7, 4, 128), (2, 4, 4, 2, 64)]:
+        T, H, W, heads, d = shape
+        inp = make_inputs(T, H, W, heads, d, "bf16", seed=50)
+        dev = to_device(inp)
+        ref, out1 = _both(dev, inp)
+        _, out2 = _both(dev, inp)
+        assert torch.equal(_bits(out1), _bits(ref)), shape
+        assert torch.equal(_bits(out2), _bits(ref)), shape
+
+
+def test_noalloc_too_large_is_rejected_before_launch():
+    """A call needing more than the 64 MiB static buffer returns
+    GLA_ERR_TOO_LARGE and leaves the output untouched."""
+    import torch
+    import gated_bidirectional_linear_amd as gla
+    heads, d = 1024, 128
+    q = torch.zeros((32, heads, d), dtype=torch.bfloat16, device="cuda")
+    beta = torch.zeros((32, heads), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(d, device="cuda")
+    out = torch.full_like(q, 3.0)
+    with pytest.raises(gla.GlaError) as e:
+        gla.forward_noalloc(q, q, q, beta, q, w, (2, 4, 4), out=out)
+    assert e.value.status == -9
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
