@@ -217,6 +217,7 @@ PLAN_KNOBS = {
     "pass2_workgroups": 3,
     "rope_global": 4,
     "token_causal_workgroups": 5,
+    "pass2_heads": 6,
 }
 
 

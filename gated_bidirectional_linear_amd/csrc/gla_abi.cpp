@@ -38,6 +38,12 @@ constexpr int kDefaultTargetWg2 = 2048;
 constexpr int kPair2Slots = 512;
 constexpr int kPair2MinTiles = 3;
 constexpr int kPair2LongChunk = 2048;
+// The four-head output kernel (bf16, d = 128, heads divisible by 4) runs one
+// workgroup of 16 waves per CU: its launch aims for one round of 256
+// workgroups, with chunks of at least kQuad2MinTiles tiles (each workgroup
+// first reads its four heads' 128 KB of bf16 state).
+constexpr int kQuad2Slots = 256;
+constexpr int kQuad2MinTiles = 2;
 
 // Launch-plan overrides (include/gla_internal.h): process-wide, 0 = the
 // measured default.  Every call reads them once, into a Knobs snapshot, so a
@@ -133,10 +139,20 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // instantiation spills registers at two workgroups per CU and measured slower than the
   // one-head kernel, so fp8 keeps the one-head kernel.
   // heads per workgroup of pass 2: pairs for bf16, d = 128 and an even head count
-  G.pass2_pair = (bf16_io && d == 128 && heads % 2 == 0 && !token_causal && !kn.on(GLA_PLAN_PASS2_GENERIC)) ? 2 : 0;
+  // heads per workgroup: four where the head count allows, else pairs (the knob caps it)
+  const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, 4);
+  G.pass2_pair = 0;
+  if (bf16_io && d == 128 && !token_causal) {
+    if (heads % 4 == 0 && max_hp >= 4) G.pass2_pair = 4;
+    else if (heads % 2 == 0 && max_hp >= 2) G.pass2_pair = 2;
+  }
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
   int want2 = ceil_div(kn.get(GLA_PLAN_PASS2_WORKGROUPS, kDefaultTargetWg2), per_seg_units2);
-  if (G.pass2_pair && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
+  if (G.pass2_pair == 4 && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
+    want2 = kQuad2Slots / per_seg_units2;   // chunks per segment in one round
+    const int most = ceil_div(tiles_per_seg, kQuad2MinTiles);
+    if (want2 > most) want2 = most;
+  } else if (G.pass2_pair && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
     want2 = kPair2Slots / per_seg_units2;   // chunks per segment in one round
     if (want2 < 1) want2 = 1;
     if ((long)ceil_div(tiles_per_seg, want2) * kTile > kPair2LongChunk) want2 = 2 * kPair2Slots / per_seg_units2;
@@ -154,7 +170,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     G.chunk2 = G.seg_len;
     G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
     // head pairs (bf16 operands, d = 128, even head count): 512-byte row segments
-    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && !kn.on(GLA_PLAN_PASS2_GENERIC)) ? 2 : 0;
+    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && max_hp >= 2) ? 2 : 0;
   }
   if (kn.on(GLA_PLAN_ROPE_GLOBAL)) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
@@ -306,7 +322,8 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   const size_t sz = (size_t)d * d + d;
   const size_t part_bytes = align256((size_t)heads * G.nseg * G.cps1 * sz * 4);
   const size_t state_bytes = align256((size_t)G.nseg * heads * sz * 4);
-  const size_t scratch_bytes = rope_bytes + part_bytes + state_bytes;
+  const size_t sbf_bytes = G.pass2_pair == 4 ? align256((size_t)G.nseg * heads * d * d * 2) : 0;
+  const size_t scratch_bytes = rope_bytes + part_bytes + state_bytes + sbf_bytes;
   if (fixed != nullptr && scratch_bytes > fixed->bytes) return GLA_ERR_TOO_LARGE;
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -336,6 +353,7 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   a.rope = reinterpret_cast<float2*>(base);
   a.partial = reinterpret_cast<float*>(base + rope_bytes);
   a.states = reinterpret_cast<float*>(base + rope_bytes + part_bytes);
+  a.states_bf16 = sbf_bytes ? reinterpret_cast<unsigned short*>(base + rope_bytes + part_bytes + state_bytes) : nullptr;
   a.dtype = dtype;
   a.stream = hs;
   a.geo = G;

@@ -59,9 +59,10 @@ struct Geometry {
   int rope_lds1;  // pass 1 stages its RoPE table rows in LDS (else reads the global table)
   int rope_lds2;  // same for pass 2
   int pass1_reg;  // pass 1 uses the register-accumulating kernel (bf16, d = 128, RoPE rows in LDS)
-  int pass2_pair; // heads per workgroup of the multi-head pass-2 kernels: 0 (one head) or 2 (bf16,
+  int pass2_pair; // heads per workgroup of the multi-head pass-2 kernels: 0 (one head), 2 (bf16,
                   // d = 128, even head count, RoPE rows in LDS; the token-causal walk takes pairs
-                  // for bf16/fp8 operands at d = 128)
+                  // for bf16/fp8 operands at d = 128) or 4 (bf16, d = 128, head count divisible
+                  // by 4, RoPE rows in LDS; reads the bf16 copy of the states)
   int t_offset;   // absolute frame of the call's frame 0 (RoPE positions only)
   int token_causal;   // token-level causal form: segments of seg_len tokens walked in order
   int include_self;   // token-causal: token i reads tokens j <= i (1) or j < i (0)
@@ -80,6 +81,8 @@ struct LaunchArgs {
   float2* rope;       // scratch: RoPE table
   float* partial;     // scratch: [heads][nseg*cps1][d*d + d]
   float* states;      // scratch: [nseg][heads][d*d + d]
+  unsigned short* states_bf16;  // scratch: [nseg][heads][d*d], S of `states` rounded to bf16
+                                // (written by the reduce kernel when pass2_pair == 4, else nullptr)
   int dtype;          // GLA_DTYPE_* of q, k, v, g, beta, out
   hipStream_t stream;
   Geometry geo;

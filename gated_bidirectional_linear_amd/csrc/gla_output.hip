@@ -510,11 +510,300 @@ __global__ __launch_bounds__(pair2::Cfg<HP>::THREADS) __attribute__((amdgpu_wave
   }
 }
 
+// ===========================================================================
+// Fused output for bf16, d = 128, four heads per workgroup, with the work split
+// by wave role.
+//
+// Four heads make each token's row segment 1 KB, so every wave instruction of
+// the row streams reads or writes one whole contiguous kilobyte (a copy with
+// this shape runs ~10% faster than with the 512-byte segments of head pairs).
+// The 16 waves of the workgroup (one workgroup per CU) take two roles:
+//   - 8 MFMA waves, two per head: wave w holds v rows 64 (w % 2) .. + 63 of
+//     head w / 2's state as bf16 16x16x32 A-fragments (64 VGPRs, read as the
+//     bf16 copy the reduce kernel writes), multiplies them by the tile's
+//     rotated queries from LDS and writes the numerators to LDS; they also
+//     load the g rows and write sigmoid(g) to LDS as fp16;
+//   - 8 stream waves: wave w takes token w of every 8-token round (lane l:
+//     head l / 16, channels 8 (l % 16) .. + 7), loads the q rows, builds
+//     R phi(q) and the denominator, and in the epilogue forms
+//     y = sigmoid(g) * num, the output RMSNorm and the store.
+// Tiles are 16 tokens; the rotated queries, the numerators and the gates are
+// double-buffered in LDS, so in one step the MFMA waves work on tile i while
+// the stream waves finish tile i - 1 and prepare tile i + 1, with one barrier
+// per step.  Since different waves carry the MFMAs and the vector work, the
+// two overlap on every SIMD instead of alternating in lockstep phases.  The
+// per-token LDS strides are odd multiples of 16 bytes, so the MFMA waves'
+// 16-token accesses hit distinct banks.  The gate goes through LDS as fp16
+// (relative rounding <= 2^-11, far below the output's bf16 rounding).
+// The per-token math is output_kernel's.
+// ===========================================================================
+namespace quad2 {
+constexpr int D = 128, HP = 4, TILE = 16;
+constexpr int NMW = 8, NSW = 8;                        // MFMA waves (two per head), stream waves
+constexpr int THREADS = 64 * (NMW + NSW);
+constexpr int TPI = NSW;                               // tokens per round: one stream wave per token row
+constexpr int TPT = TILE / TPI;                        // tokens per stream thread per tile
+constexpr int QDEPTH = 2, GDEPTH = 2;                  // tiles of q / g rows in flight
+constexpr int RQ_PITCH = D + 8;                        // 16-bit elements per (token, head) row of rq and sig
+constexpr int NUM_PITCH = D + 4;                       // floats per (token, head) row of nums
+constexpr int TOKQ = HP * RQ_PITCH + 8;                // 16-bit elements per token (69 x 16 bytes)
+constexpr int TOKN = HP * NUM_PITCH + 4;               // floats per token (133 x 16 bytes)
+constexpr int RQ_BYTES = TILE * TOKQ * 2;              // one buffer
+constexpr int NUM_BYTES = TILE * TOKN * 4;
+constexpr int SMEM = 2 * RQ_BYTES + 2 * NUM_BYTES + 2 * RQ_BYTES + kRopeLdsEntries * 8;
+static_assert(SMEM <= 160 * 1024, "LDS budget");
+}  // namespace quad2
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void output_quad_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ g, const float* __restrict__ states,
+    const bf16_t* __restrict__ states_bf16, const float* __restrict__ rms_w, const float2* __restrict__ rope,
+    bf16_t* __restrict__ out, Geometry G) {
+  using namespace quad2;
+  using R = Rope<D>;
+  constexpr int SZ = D * D + D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  bf16_t* rqs = reinterpret_cast<bf16_t*>(smem);                                    // [2][TILE][TOKQ]
+  float* nums = reinterpret_cast<float*>(smem + 2 * RQ_BYTES);                      // [2][TILE][TOKN]
+  uint16_t* sigs = reinterpret_cast<uint16_t*>(smem + 2 * RQ_BYTES + 2 * NUM_BYTES);  // [2][TILE][TOKQ] fp16
+  float2* ropel = reinterpret_cast<float2*>(smem + 4 * RQ_BYTES + 2 * NUM_BYTES);
+
+  // chunk-major over head quads: consecutive ids take the same token range
+  const int nquads = G.heads / HP;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int ci = lin / nquads;
+  const int quad = lin - ci * nquads;
+  const int seg = ci / G.cps2;
+  long s0, s1;
+  seg_bounds(G, seg, s0, s1);
+  const long cbeg = min(s0 + (long)(ci - seg * G.cps2) * G.chunk2, s1);
+  const long cend = min(cbeg + (long)G.chunk2, s1);
+  const int h0 = HP * quad;
+  const int ntiles = (int)((cend - cbeg + TILE - 1) / TILE);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  // row layout (both roles): wave w % 8 takes token w % 8 of each round; lane -> head lane / 16,
+  // channels 8 (lane % 16) .. + 7
+  const int rw = wave & 7;
+  const int hl = lane >> 4;
+  const int c16 = lane & 15;
+  // Tile loads and stores go through buffer resources based at the tile's first
+  // row and this quad, ending at the chunk's last row: rows past it read as zero
+  // and stores to them are dropped.
+  const uint32_t ROW = (uint32_t)G.heads * D * 2;
+  const uint32_t quad_off = (uint32_t)h0 * D * 2;
+  auto tile_rsrc = [&](const void* p, long t0) {
+    const long left = cend - t0;
+    const uint32_t rows = left <= 0 ? 0u : (left >= TILE ? (uint32_t)TILE : (uint32_t)left);
+    const uint32_t bytes = rows == 0 ? 0u : rows * ROW - quad_off;   // the last row ends at this quad's channels
+    return make_rsrc(reinterpret_cast<const char*>(p) + (size_t)t0 * ROW + quad_off, bytes);
+  };
+  uint32_t voff[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + rw) * ROW + (uint32_t)hl * D * 2 + 16u * c16;
+
+  const typename R::View rv = rope_view<D, true>(ropel, rope, G, cbeg, cend);
+
+  if (wave < NMW) {
+    // ------------------------------ MFMA waves ------------------------------
+    const int m = wave >> 1;            // head within the quad
+    const int vh = 64 * (wave & 1);     // first v row of this wave
+    const int r16 = lane & 15, k8 = lane >> 4;
+    u32x4 gr[GDEPTH][TPT];
+    auto issue_g = [&](u32x4 (&r)[TPT], long t0) {
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, t0);
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+    };
+#pragma unroll
+    for (int d = 0; d < GDEPTH; ++d) issue_g(gr[d], cbeg + d * TILE);
+    // A[i = v row vh + 16 mt + r16][k = 32 ks + 8 k8 + j] of the 16x16x32 MFMA
+    const bf16_t* Sb = states_bf16 + ((size_t)seg * G.heads + h0 + m) * (D * D);
+    bf16x8_t sf[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sf[mt][ks] = __builtin_bit_cast(bf16x8_t,
+                                        *reinterpret_cast<const u32x4*>(Sb + (size_t)(vh + 16 * mt + r16) * D + 32 * ks + 8 * k8));
+    lds_barrier();   // RoPE rows staged
+    lds_barrier();   // rq of tile 0 written
+    for (int i0 = 0; i0 < ntiles; i0 += GDEPTH) {
+#pragma unroll
+      for (int d = 0; d < GDEPTH; ++d) {
+        const int i = i0 + d;
+        if (i >= ntiles) break;   // uniform over the workgroup
+        const long t0 = cbeg + (long)i * TILE;
+        // numerators of tile i: num^T = S RQ^T, D[v = vh + 16 mt + 4 k8 + r][token r16]
+        const bf16_t* rqb = rqs + (size_t)(i & 1) * (TILE * TOKQ);
+        float* nb = nums + (size_t)(i & 1) * (TILE * TOKN);
+        bf16x8_t bfr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          bfr[ks] = __builtin_bit_cast(bf16x8_t,
+                                       *reinterpret_cast<const u32x4*>(rqb + r16 * TOKQ + m * RQ_PITCH + 32 * ks + 8 * k8));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mt][ks], bfr[ks], acc, 0, 0, 0);
+          *reinterpret_cast<f32x4*>(nb + r16 * TOKN + m * NUM_PITCH + vh + 16 * mt + 4 * k8) = acc;
+        }
+        // sigmoid(g) of tile i, row layout, fp16
+        uint16_t* sb = sigs + (size_t)(i & 1) * (TILE * TOKQ);
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+          float gv[8];
+          Elem<bf16_t>::unpack(gr[d][j], gv);
+          uint32_t w[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float s0 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c]));
+            const float s1 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c + 1]));
+            w[c] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){s0, s1}, f16x2_t));
+          }
+          *reinterpret_cast<u32x4*>(sb + (j * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) = (u32x4){w[0], w[1], w[2], w[3]};
+        }
+        issue_g(gr[d], t0 + GDEPTH * TILE);
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ------------------------------ stream waves ------------------------------
+  const float* zrow = states + ((size_t)seg * G.heads + h0 + hl) * SZ + D * D;
+  float zc[8], wc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    zc[c] = zrow[8 * c16 + c];
+    wc[c] = rms_w[8 * c16 + c];
+  }
+  const int t_last = cbeg < cend ? (int)((cend - 1) / (G.H * G.W)) : 0;
+  const int p0 = 4 * c16;   // this thread's 4 pairs share one axis
+  const int axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
+  const int rbase = axis == 0 ? p0 - rv.t_lo * R::PT
+                  : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
+  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+  const int HW = G.H * G.W;
+  GridPos pos;   // of token rw of the next tile to prepare; a thread's tokens are TPI apart
+  pos.set((int)min(cbeg + rw, (long)G.N - 1), G.H, G.W);
+  const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
+  const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
+
+  u32x4 qr[QDEPTH][TPT];
+  auto issue_q = [&](u32x4 (&r)[TPT], long t0) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+  };
+#pragma unroll
+  for (int d = 0; d < QDEPTH; ++d) issue_q(qr[d], cbeg + d * TILE);
+
+  float den[2][TPT];   // denominators of the tiles in flight, by parity
+  // R phi(q) of a tile into rq buffer b (bf16) and its denominators
+  auto features = [&](u32x4 (&qt)[TPT], int b) {
+    GridPos pp = pos;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tc = pp.t < t_last ? pp.t : t_last;
+      const int ps = axis == 0 ? tc : (axis == 1 ? pp.y : pp.x);
+      const f32x4* e = reinterpret_cast<const f32x4*>(rv.tab + rbase + ps * rstride);
+      const f32x4 ca = e[0], cb = e[1];
+      typename R::CS cs;
+      cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
+      cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
+      pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
+      const u32x4 u = qt[i];
+      float ss = dot2sq(u.x, 0.f);
+      ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
+      const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
+      float ph[8];
+      Elem<bf16_t>::unpack(rl, ph);
+      float dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
+      ss = group_sum<16>(ss);
+      dp = group_sum<16>(dp);
+      const float ms = ss * (1.0f / D) + G.eps;
+      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
+      den[b][i] = dp + G.eps * r;
+      R::apply(ph, cs);
+      *reinterpret_cast<u32x4*>(rqs + (size_t)b * (TILE * TOKQ) + (i * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) =
+          Elem<bf16_t>::pack(ph);
+    }
+    pos.advance(t_dt, t_dy, t_dx, G.H, G.W);
+  };
+  // gate, RMSNorm and store of the tile at t0 from buffers b
+  auto epilogue = [&](int b, long t0) {
+    const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
+    const float* nb = nums + (size_t)b * (TILE * TOKN);
+    const uint16_t* sb = sigs + (size_t)b * (TILE * TOKQ);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tok = i * TPI + rw;
+      const float* src = nb + tok * TOKN + hl * NUM_PITCH + 8 * c16;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(src + 4);
+      const u32x4 sw = *reinterpret_cast<const u32x4*>(sb + tok * TOKQ + hl * RQ_PITCH + 8 * c16);
+      const float nm[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
+      const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+      float y[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {   // sigmoid(g) * num, one v_fma_mix_f32 each
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, sv[c]);
+        y[2 * c] = fmaf((float)h.x, nm[2 * c], 0.0f);
+        y[2 * c + 1] = fmaf((float)h.y, nm[2 * c + 1], 0.0f);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss += y[c] * y[c];
+      ss = group_sum<16>(ss);
+      const float scale = out_scale(ss * (1.0f / D), den[b][i], G.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
+      buf_store16(ors, voff[i], 0, Elem<bf16_t>::pack(y));   // rows past the chunk are dropped
+    }
+  };
+
+  lds_barrier();   // RoPE rows staged
+  features(qr[0], 0);
+  issue_q(qr[0], cbeg + QDEPTH * TILE);
+  lds_barrier();   // rq of tile 0 written
+  // step i: the MFMA waves take tile i; the stream waves finish tile i - 1 and
+  // prepare tile i + 1 (past the chunk its rows read as zero)
+  for (int i0 = 0; i0 < ntiles; i0 += QDEPTH) {
+#pragma unroll
+    for (int d = 0; d < QDEPTH; ++d) {
+      const int i = i0 + d;
+      if (i >= ntiles) break;   // uniform over the workgroup
+      const long t0 = cbeg + (long)i * TILE;
+      if (i >= 1) epilogue((i - 1) & 1, t0 - TILE);
+      features(qr[(d + 1) % QDEPTH], (i + 1) & 1);
+      issue_q(qr[(d + 1) % QDEPTH], t0 + TILE + QDEPTH * TILE);
+      lds_barrier();
+    }
+  }
+  if (ntiles > 0) epilogue((ntiles - 1) & 1, cbeg + (long)(ntiles - 1) * TILE);
+}
+
 template <int D, typename E>
 hipError_t launch_output(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   if constexpr (D == 128 && Elem<E>::is_bf16) {
-    // the planner sets pass2_pair only for an even head count with the RoPE rows in LDS
+    // the planner sets pass2_pair to 4 only for a head count divisible by 4 (and gives
+    // states_bf16), to 2 only for an even one, both with the RoPE rows in LDS
+    if (G.pass2_pair == 4) {
+      hipLaunchKernelGGL(output_quad_kernel, dim3((G.heads / 4) * G.nseg * G.cps2), dim3(quad2::THREADS), 0, a.stream,
+                         (const bf16_t*)a.q, (const bf16_t*)a.g, (const float*)a.states, a.states_bf16, a.rms_w,
+                         (const float2*)a.rope, (bf16_t*)a.out, G);
+      return hipGetLastError();
+    }
     if (G.pass2_pair == 2) {
       hipLaunchKernelGGL((output_pair_kernel<E, 2>), dim3((G.heads / 2) * G.nseg * G.cps2),
                          dim3(pair2::Cfg<2>::THREADS), 0, a.stream, (const E*)a.q, (const E*)a.g,

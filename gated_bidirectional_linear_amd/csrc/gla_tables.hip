@@ -37,13 +37,15 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 //    prefix over the segments of a batch item on top of its carried state:
 //    inclusive of the segment (bidirectional and block-causal forms) or
 //    exclusive (the token-causal form, whose segments are walked token by
-//    token).  One thread per (state element, head, item).
+//    token).  One thread per (state element, head, item).  When sbf is given,
+//    each segment's S is also written rounded to bf16 (the operand the
+//    four-head output kernel loads as MFMA fragments).
 // ===========================================================================
 template <int D>
 __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restrict__ partial,
                                                            const float* S_in, const float* z_in,
                                                            float* __restrict__ states, float* S_out,
-                                                           float* z_out, Geometry G) {
+                                                           float* z_out, bf16_t* __restrict__ sbf, Geometry G) {
   constexpr int SZ = D * D + D;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
@@ -65,10 +67,11 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         if (s0 + i >= G.segs_item) break;
-        float* dst = states + ((size_t)(sfirst + s0 + i) * G.heads + h) * SZ + e;
-        if (G.states_exclusive) *dst = running;
+        const float before = running;
         running += x[i];
-        if (!G.states_exclusive) *dst = running;
+        const float sv = G.states_exclusive ? before : running;
+        states[((size_t)(sfirst + s0 + i) * G.heads + h) * SZ + e] = sv;
+        if (sbf != nullptr && e < D * D) sbf[((size_t)(sfirst + s0 + i) * G.heads + h) * (D * D) + e] = f2bf(sv);
       }
     }
   } else {
@@ -86,10 +89,11 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
 #pragma unroll
         for (int i = 0; i < w; ++i) v[i] += v[i + w];
       }
-      float* dst = states + ((size_t)(sfirst + s) * G.heads + h) * SZ + e;
-      if (G.states_exclusive) *dst = running;
+      const float before = running;
       running += v[0];
-      if (!G.states_exclusive) *dst = running;
+      const float sv = G.states_exclusive ? before : running;
+      states[((size_t)(sfirst + s) * G.heads + h) * SZ + e] = sv;
+      if (sbf != nullptr && e < D * D) sbf[((size_t)(sfirst + s) * G.heads + h) * (D * D) + e] = f2bf(sv);
     }
   }
   if (S_out != nullptr) {
@@ -114,7 +118,7 @@ hipError_t launch_state_reduce(const LaunchArgs& a) {
   constexpr int SZ = D * D + D;
   dim3 grid((SZ + 255) / 256, G.heads, G.batch);
   hipLaunchKernelGGL((state_reduce_kernel<D>), grid, dim3(256), 0, a.stream, (const float*)a.partial, a.S_in, a.z_in,
-                     a.states, a.S_out, a.z_out, G);
+                     a.states, a.S_out, a.z_out, (bf16_t*)a.states_bf16, G);
   return hipGetLastError();
 }
 

@@ -33,7 +33,9 @@ typedef enum {
   GLA_PLAN_ROPE_GLOBAL = 4,              /* > 0: RoPE rows read from the global table instead of LDS */
   GLA_PLAN_TOKEN_CAUSAL_WORKGROUPS = 5,  /* > 0: (head, segment) units aimed for by the token-causal
                                             walk (segment length follows from it) */
-  GLA_PLAN_NUM_KNOBS = 6
+  GLA_PLAN_PASS2_HEADS = 6,              /* > 0: at most this many heads per workgroup in the output
+                                            kernel (1, 2 or 4; default 4 for bf16 at d = 128) */
+  GLA_PLAN_NUM_KNOBS = 7
 } gla_plan_knob;
 
 /*

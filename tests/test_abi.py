@@ -234,10 +234,10 @@ def test_batch_extents_in_alias_checks(lib):
 
 def test_plan_override_argument_errors(lib):
     assert lib.gla_plan_override(-1, 1) == E_SHAPE
-    assert lib.gla_plan_override(6, 1) == E_SHAPE        # past GLA_PLAN_NUM_KNOBS
+    assert lib.gla_plan_override(7, 1) == E_SHAPE        # past GLA_PLAN_NUM_KNOBS
     assert lib.gla_plan_override(0, -1) == E_SHAPE
     assert lib.gla_plan_override(0, (1 << 24) + 1) == E_SHAPE
-    for knob in range(6):
+    for knob in range(7):
         assert lib.gla_plan_override(knob, 0) == OK
 
 

@@ -388,12 +388,73 @@ def test_one_head_output_kernel_bf16(plan, shape):
 
 @pytest.mark.parametrize("shape", [(3, 22, 40, 4, 128), (4, 6, 7, 8, 128), (2, 5, 9, 6, 128), (1, 1, 1, 4, 128)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_head_pair_output_kernel_bf16(shape):
+def test_head_pair_output_kernel_bf16(plan, shape):
     """The two-heads-per-workgroup output kernel (bf16, d = 128, even head
-    counts) on several head counts and grids, down to a single token."""
+    counts; capped at two heads per workgroup where four would divide the
+    head count) on several head counts and grids, down to a single token."""
+    plan("pass2_heads", 2)
     T, H, W, heads, d = shape
     inp = make_inputs(T, H, W, heads, d, "bf16", seed=24)
     out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
     err = rel_err(out, _oracle(inp))
     _report(f"head-pair output {shape}", err, TOL["bf16"])
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("shape", [(3, 22, 40, 4, 128), (4, 6, 7, 8, 128), (2, 5, 9, 12, 128), (1, 1, 1, 4, 128),
+                                   (5, 9, 13, 20, 128), (1, 3, 5, 8, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_head_quad_output_kernel_bf16(shape):
+    """The four-heads-per-workgroup output kernel with MFMA and stream waves
+    (bf16, d = 128, head counts divisible by 4) on ragged grids, down to a
+    single token and to chunks shorter than one 16-token tile."""
+    T, H, W, heads, d = shape
+    print(f"[case] quad output {shape}", flush=True)
+    inp = make_inputs(T, H, W, heads, d, "bf16", seed=25)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"head-quad output {shape}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("wg2", ["1", "7", "300", "5000"])
+def test_head_quad_chunking(plan, wg2):
+    """The four-head kernel with one chunk per (quad, segment) up to chunks of a
+    single 64-token tile, including chunk counts that leave some workgroups
+    without tokens."""
+    plan("pass2_workgroups", wg2)
+    inp = make_inputs(7, 11, 13, 8, 128, "bf16", seed=26)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"quad chunking {wg2}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T,H,W,heads,F", [(9, 8, 9, 4, 3), (7, 3, 5, 8, 2), (5, 4, 4, 12, 1), (5, 8, 16, 4, 2)])
+def test_head_quad_block_causal(T, H, W, heads, F):
+    """The four-head output kernel on per-block states (one segment per block
+    of frames, the last block shorter), with a prior state.  In the last case
+    the one-frame last block fills one of its segment's two chunks, so a
+    workgroup has no tokens."""
+    inp = make_inputs(T, H, W, heads, 128, "bf16", seed=27)
+    S0, z0 = make_state(heads, 128, seed=7)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F, S0, z0)
+    ro, rS, rz = _oracle_bc(inp, F, S0=S0, z0=z0)
+    err = rel_err(to_f64(out), ro)
+    _report(f"quad bc {(T, H, W, heads, F)}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+    assert rel_err(to_f64(z), rz) <= Z_TOL["bf16"]
+
+
+def test_head_quad_equals_pair_kernel_closely(plan):
+    """The four-head kernel rounds the gate to fp16 on its way through LDS; its
+    output stays within one bf16 step of the pair kernel's (same numerators)."""
+    torch = pytest.importorskip("torch")
+    inp = make_inputs(6, 11, 13, 8, 128, "bf16", seed=28)
+    dev = to_device(inp)
+    a = run_forward(dev, inp["grid"], inp["eps"]).float()
+    plan("pass2_heads", 2)
+    b = run_forward(dev, inp["grid"], inp["eps"]).float()
+    diff = (a - b).abs()
+    assert float(diff.max()) <= 2.0 ** -7 * max(1.0, float(b.abs().max()))
+    assert float((diff > 0).float().mean()) < 0.2
