@@ -36,6 +36,7 @@ __all__ = [
     "SIGNATURES",
     "timing_enable",
     "timing_read",
+    "timing_select",
     "plan_override",
     "plan_reset",
     "PLAN_KNOBS",
@@ -239,6 +240,21 @@ def timing_enable(on: bool = True) -> None:
     st = load().gla_timing_enable(1 if on else 0)
     if st != 0:
         raise GlaError(st, "gla_timing_enable")
+
+
+def timing_select(kernels=None) -> None:
+    """Time only the named kernels (gla_kernel_name names, or ids); None: all."""
+    lib = load()
+    if kernels is None:
+        mask = 0xFFFFFFFF
+    else:
+        names = [lib.gla_kernel_name(i).decode() for i in range(NUM_KERNELS)]
+        mask = 0
+        for k in kernels:
+            mask |= 1 << (names.index(k) if isinstance(k, str) else int(k))
+    st = lib.gla_timing_select(mask)
+    if st != 0:
+        raise GlaError(st, "gla_timing_select")
 
 
 def timing_read() -> dict:

@@ -35,6 +35,7 @@ SIGNATURES = {
     "gla_timing_enable": (_i, [_i]),
     "gla_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong), _i]),
     "gla_kernel_name": (ctypes.c_char_p, [_i]),
+    "gla_timing_select": (_i, [ctypes.c_uint]),
     "gla_plan_override": (_i, [_i, _i]),
 }
 

@@ -135,16 +135,18 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
   G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
 
-  // pass 2 takes heads in pairs (wider rows per workgroup) for bf16, d = 128.  Its fp8
-  // instantiation spills registers at two workgroups per CU and measured slower than the
-  // one-head kernel, so fp8 keeps the one-head kernel.
-  // heads per workgroup of pass 2: pairs for bf16, d = 128 and an even head count
-  // heads per workgroup: four where the head count allows, else pairs (the knob caps it)
-  const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, 4);
+  // Heads per workgroup of pass 2 at d = 128.  bf16: four where the head count
+  // allows (1 KB token row segments), else pairs.  fp8: one head by default.  The
+  // four-head kernel also takes fp8 rows (512-byte segments), but fp8 halves the
+  // bytes per token while the vector work stays, and there its fixed split of
+  // waves into MFMA and stream roles leaves the MFMA waves idle: 548 us against
+  // 480 us for the one-head kernel at 720p/60s (the pair kernel's fp8
+  // instantiation spilled registers).  The knob reaches the four-head fp8 kernel.
+  const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, bf16_io ? 4 : 1);
   G.pass2_pair = 0;
-  if (bf16_io && d == 128 && !token_causal) {
+  if (narrow && d == 128 && !token_causal) {   // bf16 or fp8 I/O
     if (heads % 4 == 0 && max_hp >= 4) G.pass2_pair = 4;
-    else if (heads % 2 == 0 && max_hp >= 2) G.pass2_pair = 2;
+    else if (bf16_io && heads % 2 == 0 && max_hp >= 2) G.pass2_pair = 2;
   }
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
   int want2 = ceil_div(kn.get(GLA_PLAN_PASS2_WORKGROUPS, kDefaultTargetWg2), per_seg_units2);
@@ -170,7 +172,8 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     G.chunk2 = G.seg_len;
     G.rope_lds2 = rope_fits(G.seg_len, gla::kRopeLdsEntriesCausal) ? 1 : 0;
     // head pairs (bf16 operands, d = 128, even head count): 512-byte row segments
-    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && max_hp >= 2) ? 2 : 0;
+    const int walk_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, 2);
+    G.pass2_pair = (narrow && d == 128 && heads % 2 == 0 && walk_hp >= 2) ? 2 : 0;
   }
   if (kn.on(GLA_PLAN_ROPE_GLOBAL)) G.rope_lds1 = G.rope_lds2 = 0;
   // the register-accumulating and paired-head kernels read their RoPE rows from LDS only
@@ -187,24 +190,38 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Timing-only events: no system-scope fence when they complete, so recording
 // them does not write back and invalidate the caches between the kernels they
 // bracket (the default fence added ~7 us per kernel boundary at 720p/60s).
+// Events are taken from a free list and returned to it when read, so a timed
+// call creates none once the list has grown to the calls' needs.
 struct EventTimer final : gla::Timer {
   struct Rec { int id; hipEvent_t a, b; };
   bool on = false;
+  unsigned mask = ~0u;            // kernel ids timed while on
   std::vector<Rec> recs;
   std::vector<hipEvent_t> open;   // per kernel id, start event awaiting its end
+  std::vector<hipEvent_t> pool;   // created events not in use
   std::mutex mu;
   EventTimer() : open(gla::kNumKernels, nullptr) {}
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
+    return e;
+  }
   void begin(int id, hipStream_t s) override {
-    if (!on) return;
-    hipEvent_t e;
-    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
+    if (!on || !((mask >> id) & 1u)) return;
+    hipEvent_t e = take();
+    if (e == nullptr) return;
     hipEventRecord(e, s);
     open[id] = e;
   }
   void end(int id, hipStream_t s) override {
     if (!on || open[id] == nullptr) return;
-    hipEvent_t e;
-    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
+    hipEvent_t e = take();
+    if (e == nullptr) return;
     hipEventRecord(e, s);
     recs.push_back({id, open[id], e});
     open[id] = nullptr;
@@ -497,11 +514,18 @@ int gla_timing_read(double* ms, long long* launches, int n) {
       if (ms) ms[r.id] += t;
       if (launches) launches[r.id] += 1;
     }
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    tm.pool.push_back(r.a);
+    tm.pool.push_back(r.b);
   }
   tm.recs.clear();
   return st;
+}
+
+int gla_timing_select(unsigned mask) {
+  EventTimer& tm = timer();
+  std::lock_guard<std::mutex> lk(tm.mu);
+  tm.mask = mask;
+  return GLA_OK;
 }
 
 int gla_plan_override(int knob, int value) {

@@ -558,11 +558,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// E: bf16 rows (16 bytes per lane and 8 channels) or fp8 e4m3 rows (8 bytes; a
+// token's four heads are then 512 contiguous bytes per wave instruction),
+// widened to bf16 exactly for the features.
+template <typename E>
 __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void output_quad_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ g, const float* __restrict__ states,
+    const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
     const bf16_t* __restrict__ states_bf16, const float* __restrict__ rms_w, const float2* __restrict__ rope,
-    bf16_t* __restrict__ out, Geometry G) {
+    E* __restrict__ out, Geometry G) {
   using namespace quad2;
+  using BR = BufRow<E>;
+  typedef typename BR::Raw Raw;
+  constexpr uint32_t ES = sizeof(E);
   using R = Rope<D>;
   constexpr int SZ = D * D + D;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -595,8 +602,8 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   // Tile loads and stores go through buffer resources based at the tile's first
   // row and this quad, ending at the chunk's last row: rows past it read as zero
   // and stores to them are dropped.
-  const uint32_t ROW = (uint32_t)G.heads * D * 2;
-  const uint32_t quad_off = (uint32_t)h0 * D * 2;
+  const uint32_t ROW = (uint32_t)G.heads * D * ES;
+  const uint32_t quad_off = (uint32_t)h0 * D * ES;
   auto tile_rsrc = [&](const void* p, long t0) {
     const long left = cend - t0;
     const uint32_t rows = left <= 0 ? 0u : (left >= TILE ? (uint32_t)TILE : (uint32_t)left);
@@ -605,7 +612,7 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   };
   uint32_t voff[TPT];
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + rw) * ROW + (uint32_t)hl * D * 2 + 16u * c16;
+  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + rw) * ROW + (uint32_t)hl * D * ES + 8u * ES * c16;
 
   const typename R::View rv = rope_view<D, true>(ropel, rope, G, cbeg, cend);
 
@@ -614,11 +621,11 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
     const int m = wave >> 1;            // head within the quad
     const int vh = 64 * (wave & 1);     // first v row of this wave
     const int r16 = lane & 15, k8 = lane >> 4;
-    u32x4 gr[GDEPTH][TPT];
-    auto issue_g = [&](u32x4 (&r)[TPT], long t0) {
+    Raw gr[GDEPTH][TPT];
+    auto issue_g = [&](Raw (&r)[TPT], long t0) {
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, t0);
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+      for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
     };
 #pragma unroll
     for (int d = 0; d < GDEPTH; ++d) issue_g(gr[d], cbeg + d * TILE);
@@ -659,7 +666,7 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
           float gv[8];
-          Elem<bf16_t>::unpack(gr[d][j], gv);
+          Elem<E>::unpack(gr[d][j], gv);
           uint32_t w[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -696,18 +703,18 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
   const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
 
-  u32x4 qr[QDEPTH][TPT];
-  auto issue_q = [&](u32x4 (&r)[TPT], long t0) {
+  Raw qr[QDEPTH][TPT];
+  auto issue_q = [&](Raw (&r)[TPT], long t0) {
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) r[i] = buf_load16(rs, voff[i], 0);
+    for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
   };
 #pragma unroll
   for (int d = 0; d < QDEPTH; ++d) issue_q(qr[d], cbeg + d * TILE);
 
   float den[2][TPT];   // denominators of the tiles in flight, by parity
   // R phi(q) of a tile into rq buffer b (bf16) and its denominators
-  auto features = [&](u32x4 (&qt)[TPT], int b) {
+  auto features = [&](Raw (&qt)[TPT], int b) {
     GridPos pp = pos;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -719,7 +726,13 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
       cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
       pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
-      const u32x4 u = qt[i];
+      u32x4 u;   // 8 channels as bf16 pairs (fp8 widens exactly)
+      if constexpr (sizeof(E) == 1) {
+        u = (u32x4){Elem<fp8_t>::bf16_pair<false>(qt[i].x), Elem<fp8_t>::bf16_pair<true>(qt[i].x),
+                    Elem<fp8_t>::bf16_pair<false>(qt[i].y), Elem<fp8_t>::bf16_pair<true>(qt[i].y)};
+      } else {
+        u = qt[i];
+      }
       float ss = dot2sq(u.x, 0.f);
       ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
       const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
@@ -767,7 +780,7 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       const float scale = out_scale(ss * (1.0f / D), den[b][i], G.eps);
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
-      buf_store16(ors, voff[i], 0, Elem<bf16_t>::pack(y));   // rows past the chunk are dropped
+      BR::store(ors, voff[i], 0, Elem<E>::pack(y));   // rows past the chunk are dropped
     }
   };
 
@@ -795,15 +808,17 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
 template <int D, typename E>
 hipError_t launch_output(const LaunchArgs& a) {
   const Geometry& G = a.geo;
-  if constexpr (D == 128 && Elem<E>::is_bf16) {
-    // the planner sets pass2_pair to 4 only for a head count divisible by 4 (and gives
-    // states_bf16), to 2 only for an even one, both with the RoPE rows in LDS
+  if constexpr (D == 128 && sizeof(E) <= 2) {
+    // the planner sets pass2_pair to 4 (bf16 or fp8) only for a head count divisible by 4
+    // (and gives states_bf16), to 2 (bf16) only for an even one, both with the RoPE rows in LDS
     if (G.pass2_pair == 4) {
-      hipLaunchKernelGGL(output_quad_kernel, dim3((G.heads / 4) * G.nseg * G.cps2), dim3(quad2::THREADS), 0, a.stream,
-                         (const bf16_t*)a.q, (const bf16_t*)a.g, (const float*)a.states, a.states_bf16, a.rms_w,
-                         (const float2*)a.rope, (bf16_t*)a.out, G);
+      hipLaunchKernelGGL((output_quad_kernel<E>), dim3((G.heads / 4) * G.nseg * G.cps2), dim3(quad2::THREADS), 0,
+                         a.stream, (const E*)a.q, (const E*)a.g, (const float*)a.states, a.states_bf16, a.rms_w,
+                         (const float2*)a.rope, (E*)a.out, G);
       return hipGetLastError();
     }
+  }
+  if constexpr (D == 128 && Elem<E>::is_bf16) {
     if (G.pass2_pair == 2) {
       hipLaunchKernelGGL((output_pair_kernel<E, 2>), dim3((G.heads / 2) * G.nseg * G.cps2),
                          dim3(pair2::Cfg<2>::THREADS), 0, a.stream, (const E*)a.q, (const E*)a.g,

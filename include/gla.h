@@ -257,6 +257,10 @@ int gla_version(void);
 int gla_timing_enable(int on);
 int gla_timing_read(double* ms, long long* launches, int n);
 const char* gla_kernel_name(int kernel_id);
+/* Which kernels the timing records: bit i of mask selects kernel id i (all
+ * by default).  Each timed kernel adds an event pair to the call's stream,
+ * so timing fewer kernels disturbs the calls less.  Returns GLA_OK. */
+int gla_timing_select(unsigned mask);
 
 #ifdef __cplusplus
 }

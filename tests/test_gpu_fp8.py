@@ -31,7 +31,7 @@ def _report(name, err):
 
 
 @pytest.mark.parametrize("shape", [(2, 4, 4, 2, 32), (1, 1, 1, 3, 64), (3, 5, 7, 2, 64), (5, 9, 13, 3, 128),
-                                   (4, 16, 16, 2, 128), (9, 15, 26, 2, 64)],
+                                   (4, 16, 16, 2, 128), (9, 15, 26, 2, 64), (5, 9, 13, 4, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_fp8_shapes(shape):
     T, H, W, heads, d = shape
@@ -134,3 +134,51 @@ def test_fp8_binding_rejects_mixed_dtypes():
     dev["g"] = dev["g"].to(torch.bfloat16)
     with pytest.raises(TypeError):
         gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"])
+
+
+@pytest.mark.parametrize("d", [128])
+def test_fp8_every_gate_code_four_heads(plan, d):
+    """Every finite e4m3 gate code through the four-head output kernel (chosen
+    by the plan knob: the one-head kernel is the fp8 default), whose MFMA waves
+    compute sigmoid(g) and pass it to the stream waves as fp16."""
+    plan("pass2_heads", 4)
+    T, H, W, heads = 4, 8, 9, 4
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=42)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    n = inp["g_bits"].size
+    bits = np.resize(np.random.default_rng(6).permutation(codes), n).reshape(inp["g_bits"].shape)
+    inp["g_bits"] = bits
+    inp["g"] = fp8_bits_to_f32(bits)
+    got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = fp8_excess(got, _oracle(inp))
+    _report(f"every gate code, four heads, d={d}", err)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("shape", [(5, 9, 13, 4, 128), (1, 1, 1, 8, 128), (2, 5, 9, 12, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_four_head_kernel_shapes(plan, shape):
+    """The four-head output kernel on fp8 rows (512-byte token segments)."""
+    plan("pass2_heads", 4)
+    T, H, W, heads, d = shape
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=44)
+    got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = fp8_excess(got, _oracle(inp))
+    _report(f"four-head kernel {shape}", err)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL["fp8"]
+
+
+def test_fp8_block_causal_four_heads(plan):
+    """Block-causal fp8 with 8 heads: per-block states through the four-head kernel."""
+    plan("pass2_heads", 4)
+    T, H, W, heads, d, F = 7, 6, 7, 8, 128, 3
+    inp = make_inputs(T, H, W, heads, d, "fp8", seed=43)
+    S0, z0 = make_state(heads, d, seed=8)
+    out, S, z = run_block_causal(to_device(inp), inp["grid"], inp["eps"], F, S0, z0)
+    ro, rS, rz = _oracle_bc(inp, F, S0=S0, z0=z0)
+    err = fp8_excess(to_f64(out), ro)
+    _report(f"block-causal four heads {(T, H, W, heads, F)}", err)
+    assert err <= TOL["fp8"]
+    assert rel_err(to_f64(z), rz) <= Z_TOL["fp8"]
