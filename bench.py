@@ -155,17 +155,30 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, worklo
         print(f"wrote {path}: {(fetched + written) / 1e9:.3f} GB per launch")
 
 
-def write_mfma_summary(pmc_csv: str, workload: str, commands: str, token_causal: bool = False,
-                       num_cu: int = 256, num_xcd: int = 8) -> None:
-    """MFMA busy fraction per kernel from a rocprofv3 counter run of
-    SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over every SIMD: 32 per
-    32x32x16 bf16 MFMA) and GRBM_GUI_ACTIVE (active cycles summed over the
-    XCDs): busy / (GRBM_GUI_ACTIVE / XCDs x CUs x 4 SIMDs).  The active cycles
-    over the dispatch's duration give the clock the kernel ran at."""
+SQ_COUNTERS = ("SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_LDS "
+               "SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def write_sq_summary(pmc_csv: str, workload: str, commands: str, token_causal: bool = False,
+                     num_cu: int = 256, num_xcd: int = 8) -> None:
+    """Per-kernel issue summary from one rocprofv3 counter run of SQ_COUNTERS.
+
+    cycles = GRBM_GUI_ACTIVE / XCDs (the dispatch's clock cycles; the counter is
+    summed over the 8 XCDs).  Per-SIMD fractions divide a chip-wide sum by
+    cycles x CUs x 4 SIMDs:
+      valu      = 4 SQ_ACTIVE_INST_VALU (quad-cycles that waves spend issuing
+                  vector instructions, summed over waves; two waves of one SIMD
+                  can count in the same cycle, so this can exceed 1)
+      mfma      = SQ_VALU_MFMA_BUSY_CYCLES (32 busy cycles per 32x32x16 MFMA)
+      coexec    = SQ_VALU_MFMA_COEXEC_CYCLES (cycles in which a vector
+                  instruction issued while the matrix unit was busy)
+      lds       = 4 SQ_ACTIVE_INST_LDS, lds_wait = 4 SQ_WAIT_INST_LDS (summed over waves)
+    bank_conflicts is SQ_LDS_BANK_CONFLICT per dispatch (cycles, chip-wide);
+    clock = cycles / dispatch duration."""
     import collections
     import csv
-    busy = _pmc_means(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
-    active = _pmc_means(pmc_csv, "GRBM_GUI_ACTIVE")
+    names = SQ_COUNTERS.split()
+    means = {n: _pmc_means(pmc_csv, n) for n in names}
     dur = collections.defaultdict(list)
     seen = set()
     for r in csv.DictReader(open(pmc_csv)):
@@ -173,22 +186,35 @@ def write_mfma_summary(pmc_csv: str, workload: str, commands: str, token_causal:
             continue
         seen.add(r["Dispatch_Id"])
         dur[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"sq_{workload}.txt")
     with open(path, "w") as f:
-        f.write(f"# MFMA busy fraction per kernel on the {workload} workload, from rocprofv3 counters\n")
+        f.write(f"# SQ issue counters per kernel on the {workload} workload, from one rocprofv3 counter run\n")
         f.write("# commands:\n")
         for line in commands.strip().splitlines():
             f.write(f"#   {line}\n")
-        f.write(f"# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {num_xcd} XCDs x {num_cu} CUs x 4 SIMDs);\n")
-        f.write("# clock = GRBM_GUI_ACTIVE / XCDs / dispatch duration (means over dispatches)\n")
-        for k in sorted(busy):
-            if not k.removeprefix("void ").startswith("gla::") or not active.get(k):
+        f.write(f"# cycles = GRBM_GUI_ACTIVE / {num_xcd}; per-SIMD fractions = chip-wide sum / "
+                f"(cycles x {num_cu} CUs x 4 SIMDs):\n")
+        f.write("# valu = 4 SQ_ACTIVE_INST_VALU (summed over waves), mfma = SQ_VALU_MFMA_BUSY_CYCLES,\n"
+                "# coexec = SQ_VALU_MFMA_COEXEC_CYCLES, lds = 4 SQ_ACTIVE_INST_LDS, lds_wait = 4 SQ_WAIT_INST_LDS;\n"
+                "# bank_conflicts = SQ_LDS_BANK_CONFLICT per dispatch; means over dispatches\n")
+        f.write(f"{'kernel':56s} {'valu':>6s} {'mfma':>6s} {'coexec':>6s} {'lds':>6s} {'ldswait':>7s} "
+                f"{'bankconf':>9s} {'clock':>9s}\n")
+        for k in sorted(means["GRBM_GUI_ACTIVE"]):
+            if not k.removeprefix("void ").startswith("gla::"):
                 continue
-            cycles = active[k] / num_xcd
-            frac = busy[k] / (cycles * num_cu * 4)
+            cyc = means["GRBM_GUI_ACTIVE"][k] / num_xcd
+            if cyc <= 0:
+                continue
+            simd = cyc * num_cu * 4
             ns = sum(dur[k]) / len(dur[k]) if dur.get(k) else 0.0
-            clock = f"{cycles / ns:5.2f} GHz" if ns > 50_000 else "n/a (short dispatch)"
-            f.write(f"{k.removeprefix('void ').split('(')[0][:60]:60s} mfma_busy {frac:7.4f}  clock {clock}\n")
+            clock = f"{cyc / ns:5.2f} GHz" if ns > 50_000 else "n/a"
+            f.write(f"{k.removeprefix('void ').split('(')[0][:56]:56s} "
+                    f"{4 * means['SQ_ACTIVE_INST_VALU'].get(k, 0) / simd:6.3f} "
+                    f"{means['SQ_VALU_MFMA_BUSY_CYCLES'].get(k, 0) / simd:6.3f} "
+                    f"{means['SQ_VALU_MFMA_COEXEC_CYCLES'].get(k, 0) / simd:6.3f} "
+                    f"{4 * means['SQ_ACTIVE_INST_LDS'].get(k, 0) / simd:6.3f} "
+                    f"{4 * means['SQ_WAIT_INST_LDS'].get(k, 0) / simd:7.3f} "
+                    f"{means['SQ_LDS_BANK_CONFLICT'].get(k, 0):9.3g} {clock:>9s}\n")
         f.write(f"kernel_source_sha256: {kernel_source_hash(token_causal)}\n")
     print(f"wrote {path}")
 
@@ -369,15 +395,19 @@ def main(argv=None):
                          "kernel_stats.csv")
     ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
     ap.add_argument("--stats-bench-log", default="", help="output of the profiled bench.py run (its JSON line)")
-    ap.add_argument("--mfma-summary", metavar="COUNTER_CSV",
-                    help="CPU only: write the MFMA busy summary under profiles/ from a rocprofv3 "
-                         "counter_collection.csv of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
+    ap.add_argument("--sq-summary", metavar="COUNTER_CSV",
+                    help="CPU only: write the SQ issue summary under profiles/ from a rocprofv3 "
+                         "counter_collection.csv of the counters in SQ_COUNTERS")
     args = ap.parse_args(argv)
 
     token_causal = args.form != "workload"
-    label = args.workload + ("_token_causal" if token_causal else "")   # names the profiles/ summaries
-    if args.mfma_summary:
-        write_mfma_summary(args.mfma_summary, label, args.pmc_commands, token_causal)
+    # names the profiles/ summaries: workload, a dtype other than the workload's own, the form
+    from workloads import WORKLOADS as _W
+    own = _W[args.workload].dtype if args.workload in _W else None
+    label = (args.workload + (f"_{args.dtype}" if args.dtype not in (None, own) else "")
+             + ("_token_causal" if token_causal else ""))
+    if args.sq_summary:
+        write_sq_summary(args.sq_summary, label, args.pmc_commands, token_causal)
         return 0
     if args.stats_summary:
         write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal, args.warmup,
@@ -408,7 +438,7 @@ def main(argv=None):
         print("--batch must be at least 1", file=sys.stderr)
         return 2
     # profiles/ hold the default-dtype, single-sequence kernels
-    profiled = (args.dtype is None or args.dtype == w.dtype) and B == 1
+    profiled = B == 1
     if args.dtype is not None:
         import dataclasses
         w = dataclasses.replace(w, dtype=args.dtype)
