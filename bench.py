@@ -367,7 +367,8 @@ def cpu_baseline_token_causal(w, inp, include_self: bool, heads_sample: int = 2,
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50, or as many as take ~50 ms when a step is shorter than 1 ms)")
     # the clocks settle after ~20 steps (~25 ms) of load: 3 warm-up steps time
     # ~3% slower at 720p/60s, 20 or more time the same
     ap.add_argument("--warmup", type=int, default=20)
@@ -492,18 +493,24 @@ def main(argv=None):
         else:
             gla.forward(b["q"], b["k"], b["v"], b["beta"], b["g"], rms_w, grid, eps=w.eps, out=b["out"])
 
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    est = (time.perf_counter() - t_w) / max(1, args.warmup)   # seconds per step, roughly
+    if args.steps is None:
+        args.steps = 50 if est >= 1e-3 else max(50, min(5000, int(0.05 / max(est, 1e-6))))
+    # HIP event pairs around one kernel per sampled step, kernels in rotation:
+    # every step when steps are long, every 8th step when they are short (a
+    # pair adds ~5 us to a 56 us step at 480p, and none measurably to 1 ms)
+    period = 1 if est >= 5e-4 else 8
     gla.timing_read()            # discard anything recorded before
     gla.timing_enable(True)
     torch.cuda.synchronize()
-    # Each timed step records one HIP event pair, around one kernel: kernel
-    # i % 4 on step i, so every kernel is sampled over the timed region while
-    # each step carries the overhead of only two events.
     t_start = time.perf_counter()
     for i in range(args.steps):
-        gla.timing_select([i % gla.NUM_KERNELS])
+        gla.timing_select([(i // period) % gla.NUM_KERNELS] if i % period == 0 else [])
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -588,7 +595,10 @@ def main(argv=None):
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "alg_bytes_per_step": alg_step,
         "kernels": kernels,
-        "kernel_timing": "HIP events around one kernel per timed step (kernel i % 4 on step i)",
+        "kernel_timing": ("HIP events around one kernel on " + ("every timed step" if period == 1 else
+                          f"every {period}th timed step") + ", the four kernels in rotation; launches timed per "
+                          "kernel: "
+                          + ", ".join(f"{k} {v[1]}" for k, v in kt.items())),
         "roofline": {
             "kernel": dom,
             "bound": "hbm",

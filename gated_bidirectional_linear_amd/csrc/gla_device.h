@@ -279,6 +279,74 @@ struct Rope {
     }
   }
 
+  // Frequency of pair p of the head dim: pair i of an axis of width da turns
+  // by pos * 10000^(-2i/da).
+  __device__ __forceinline__ static double freq_of(int p) {
+    const int i = p < PT ? p : (p < PT + PY ? p - PT : p - PT - PY);
+    const int da = p < PT ? D / 4 : 3 * D / 8;
+    return pow(10000.0, -2.0 * (double)i / (double)da);
+  }
+
+  // (cos a, sin a): the angle in fp64, reduced to [-pi, pi] in fp64 (2 pi as
+  // a two-term sum), then sine and cosine of the reduced angle in fp32 (the
+  // table stores fp32).  Exact to the last bits of fp32 for positions up to
+  // 2^31.
+  __device__ __forceinline__ static float2 cos_sin(double a) {
+    const double k = rint(a * 0.15915494309189535);
+    double r = fma(-k, 6.283185307179586, a);
+    r = fma(-k, 2.4492935982947064e-16, r);
+    float s, c;
+    sincosf((float)r, &s, &c);
+    return make_float2(c, s);
+  }
+
+  // Position and pair of entry e of a table laid out as frames [t_lo, t_lo +
+  // nt) ([nt][PT]), then [H][PY], then [W][PX].  Frame row t (of the batch's
+  // frame rows) holds item frame t % T_item at absolute frame t_offset + that.
+  __device__ __forceinline__ static void entry_pos(int e, int t_lo, int nt, int H, int T_item, int t_offset,
+                                                   long& pos, int& p) {
+    const int n_t = nt * PT;
+    if (e < n_t) {
+      pos = (long)((t_lo + e / PT) % T_item) + t_offset;
+      p = e % PT;
+    } else if (e < n_t + H * PY) {
+      const int r = e - n_t;
+      pos = r / PY;
+      p = PT + r % PY;
+    } else {
+      const int r = e - n_t - H * PY;
+      pos = r / PX;
+      p = PT + PY + r % PX;
+    }
+  }
+
+  // Compute the frames [t_lo, t_lo + nt) and the y/x blocks of the table into
+  // LDS as put(index, (cos, sin)), and write them to the global table `tab`
+  // ([T][PT], [H][PY], [W][PX]) for the later kernels: the frame rows always
+  // (workgroups whose chunks share a frame write the same bits), the y/x blocks
+  // when write_yx.  freq: LDS space for D/2 doubles.  All NT threads take
+  // part; the caller synchronises before the LDS entries are read.
+  template <int kMaxEntries, int NT, typename Put>
+  __device__ __forceinline__ static void compute(Put put, double* freq, float2* __restrict__ tab, int T, int H, int W,
+                                                 int T_item, int t_offset, int t_lo, int nt, bool write_yx) {
+    const int tid = (int)threadIdx.x;
+    if (tid < D / 2) freq[tid] = freq_of(tid);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const int n_t = nt * PT;
+    const int total = n_t + H * PY + W * PX;
+    for (int e = tid; e < total && e < kMaxEntries; e += NT) {
+      long pos;
+      int p;
+      entry_pos(e, t_lo, nt, H, T_item, t_offset, pos, p);
+      const float2 cs = cos_sin((double)pos * freq[p]);
+      put(e, cs);
+      if (e < n_t) tab[(long)t_lo * PT + e] = cs;
+      else if (write_yx) tab[(long)T * PT + (e - n_t)] = cs;
+    }
+  }
+
   // Copy the frames [t_lo, t_lo + nt) and the y/x blocks of the global table
   // into LDS (all kThreads threads take part; caller synchronises).  At most
   // kMaxEntries entries; every thread issues its loads together (indices

@@ -1,6 +1,7 @@
-// Launch sequence of one operator call: RoPE table, state partials,
-// reduce/prefix, fused output (or the token-causal walk), each bracketed by
-// the optional timer.
+// Launch sequence of one operator call: RoPE table (only when pass 1 cannot
+// hold a chunk's RoPE rows in LDS; otherwise pass 1 computes the table), state
+// partials, reduce/prefix, fused output (or the token-causal walk), each
+// bracketed by the optional timer.
 #include "gla_launch.h"
 
 namespace gla {
@@ -17,10 +18,12 @@ template <int D, typename E> hipError_t launch_token_causal(const LaunchArgs& a)
 template <int D, typename E>
 static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
   hipError_t e;
-  tm.begin(0, a.stream);
-  e = launch_rope_table<D>(a);
-  tm.end(0, a.stream);
-  if (e != hipSuccess) return e;
+  if (!a.geo.rope_lds1) {   // otherwise pass 1 computes the RoPE table
+    tm.begin(0, a.stream);
+    e = launch_rope_table<D>(a);
+    tm.end(0, a.stream);
+    if (e != hipSuccess) return e;
+  }
   tm.begin(1, a.stream);
   e = launch_state_partial<D, E>(a);
   tm.end(1, a.stream);

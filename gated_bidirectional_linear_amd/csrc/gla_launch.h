@@ -9,8 +9,10 @@
 // The tokens are cut into "segments": one segment of N tokens for the
 // bidirectional form, one per block of latent frames for the block-causal
 // form, or runs of 32-token tiles sized for parallelism in the token-causal
-// form.  Four launches on the caller's stream:
-//   1. rope_table_kernel    (gla_tables.hip): per-axis cos/sin tables, fp64 angles.
+// form.  Up to four launches on the caller's stream:
+//   1. rope_table_kernel    (gla_tables.hip): per-axis cos/sin tables, fp64 angles;
+//      only when a pass-1 chunk's RoPE rows do not fit in LDS (otherwise pass 1
+//      computes them and writes the table).
 //   2. state_partial kernels (gla_state.hip): one workgroup per (head, chunk of
 //      a segment) builds the partial V^T (beta R phi K^) on MFMA with fp32
 //      accumulation, plus the partial key sum.

@@ -25,10 +25,13 @@ struct PartialCfg {
                                                        : (ZRED_BYTES > KRED_BYTES ? ZRED_BYTES : KRED_BYTES);
 };
 
+// LDSR: the chunk's RoPE rows fit in LDS; the kernel then computes them there
+// and writes them to the global table for the later kernels (no table
+// kernel runs).  Otherwise it reads the table the table kernel wrote.
 template <int D, typename E, bool LDSR>
 __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
-    const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
+    float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   using C = PartialCfg<D, E>;
   using L = typename C::L;
   using M = Mfma<L>;
@@ -65,10 +68,21 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
     for (int i = 0; i < C::TPT; ++i)
       br[i] = beta[(size_t)min(n0 + i, ch.end - 1) * G.heads + ch.head];
   };
-  const typename Rope<D>::View rv =
-      rope_view<D, LDSR>(reinterpret_cast<float2*>(smem + C::SMEM), rope, G, ch.begin, ch.end);
   if (ch.begin < ch.end) issue(ch.begin);
-  if constexpr (LDSR) lds_barrier();
+  typename Rope<D>::View rv;
+  if constexpr (LDSR) {
+    // the frequency scratch sits in the tile region, unused until the loop
+    float2* tab = reinterpret_cast<float2*>(smem + C::SMEM);
+    const int t_lo = ch.begin < ch.end ? (int)(ch.begin / HW) : 0;
+    const int nt = ch.begin < ch.end ? (int)((ch.end - 1) / HW) - t_lo + 1 : 0;
+    Rope<D>::template compute<kRopeLdsEntries, kThreads>([&](int e, float2 cs) { tab[e] = cs; },
+                                                         reinterpret_cast<double*>(smem), rope, G.T, G.H, G.W,
+                                                         G.T_item, G.t_offset, t_lo, nt, lin == 0);
+    rv = typename Rope<D>::View{tab, t_lo, nt, G.H};
+    lds_barrier();
+  } else {
+    rv = typename Rope<D>::View{rope, 0, G.T, G.H};
+  }
 
   for (long t0 = ch.begin; t0 < ch.end; t0 += kTile) {
     const long n0 = t0 + (long)tg * C::TPT;
@@ -312,27 +326,17 @@ __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
   return L;
 }
 
-// RoPE rows of the frames the chunk spans, the y block and the x block, as
-// per-pair bf16 words (cos, -sin), (sin, cos).  All threads take part; the
-// caller synchronises.
-__device__ __forceinline__ void stage_rotations(unsigned char* rtab, const float2* __restrict__ rope,
-                                                const Geometry& G, const Lane& L) {
-  constexpr int PER = kRopeLdsEntries / kThreads;
-  const int n_t = L.nt * R::PT;
-  const int total = n_t + G.H * R::PY + G.W * R::PX;
-  float2 tmp[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = (int)threadIdx.x + j * kThreads;
-    const int src = (i < n_t) ? L.t_lo * R::PT + i : G.T * R::PT + (i - n_t);
-    tmp[j] = rope[i < total ? src : 0];
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = (int)threadIdx.x + j * kThreads;
-    if (i < total)
-      *reinterpret_cast<u32x2*>(rtab + 8 * i) = (u32x2){pack2bf(tmp[j].x, -tmp[j].y), pack2bf(tmp[j].y, tmp[j].x)};
-  }
+// RoPE rows of the frames the chunk spans, the y block and the x block,
+// computed into LDS as per-pair bf16 words (cos, -sin), (sin, cos), and
+// written in fp32 to the global table for the later kernels (the y/x blocks
+// by one workgroup).  All threads take part; the caller synchronises.
+__device__ __forceinline__ void compute_rotations(unsigned char* rtab, double* freq, float2* __restrict__ rope,
+                                                  const Geometry& G, const Lane& L, bool write_yx) {
+  R::template compute<kRopeLdsEntries, kThreads>(
+      [&](int e, float2 cs) {
+        *reinterpret_cast<u32x2*>(rtab + 8 * e) = (u32x2){pack2bf(cs.x, -cs.y), pack2bf(cs.y, cs.x)};
+      },
+      freq, rope, G.T, G.H, G.W, G.T_item, G.t_offset, L.t_lo, L.nt, write_yx);
 }
 
 // bf16 pair (lo: token a, hi: token b) of channel c from two raw 4-channel rows
@@ -490,7 +494,7 @@ constexpr int kDepth = GLA_ACC_DEPTH;        // steps of rows in flight per wave
 template <typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_partial_acc_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
-    const float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
+    float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
   using namespace frag1;
   using namespace acc1;
   // the RoPE table and the final sum share LDS (the table is dead by then)
@@ -503,7 +507,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const Lane L = make_lane<E>(G, ch);
   const int HW = G.H * G.W;
-  stage_rotations(rtab, rope, G, L);
+  // the first rows are requested before the RoPE rows are computed
+  Rows<E> rr[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(rr[d], k, v, beta, ch.begin + d * kTile + wave * kStep, ch.end, G.heads, L);
+  compute_rotations(rtab, reinterpret_cast<double*>(zred), rope, G, L, lin == 0);
 
   // grid position of this lane's own token; a wave's steps are 64 apart
   GridPos gp;
@@ -550,9 +558,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  Rows<E> rr[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue(rr[d], k, v, beta, ch.begin + d * kTile + wave * kStep, ch.end, G.heads, L);
   for (long t0 = ch.begin; t0 < ch.end; t0 += kDepth * kTile) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) step(rr[d], t0 + d * kTile);
@@ -600,16 +605,16 @@ hipError_t launch_state_partial(const LaunchArgs& a) {
   if constexpr (D == 128 && Elem<typename Elem<E>::Lds>::is_bf16) {   // bf16 and fp8 rows
     if (G.pass1_reg) {   // the planner sets it only with the RoPE rows in LDS
       hipLaunchKernelGGL((state_partial_acc_kernel<E>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.k,
-                         (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
+                         (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
       return hipGetLastError();
     }
   }
   if (G.rope_lds1)
     hipLaunchKernelGGL((state_partial_kernel<D, E, true>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
+                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
   else
     hipLaunchKernelGGL((state_partial_kernel<D, E, false>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, (const float2*)a.rope, a.partial, G);
+                       (const E*)a.k, (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
   return hipGetLastError();
 }
 

@@ -10,26 +10,27 @@ namespace gla {
 template <int D>
 // Frame row t (of all T frames of the batch) holds item frame t % T_item, at
 // absolute frame t_offset + t % T_item (streaming across calls); rows and
-// columns always start at 0.
+// columns always start at 0.  The pass-1 kernels compute the same entries
+// (Rope::compute) when their rows fit in LDS; this kernel runs only when they
+// do not.
 __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int T, int H, int W, int t_offset,
                                                          int T_item) {
   using R = Rope<D>;
   const long total = (long)T * R::PT + (long)H * R::PY + (long)W * R::PX;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  long pos, i;
-  int da;
+  long pos;
+  int p;   // pair of the head dim
   if (idx < (long)T * R::PT) {
-    pos = (idx / R::PT) % T_item + t_offset; i = idx % R::PT; da = D / 4;
+    pos = (idx / R::PT) % T_item + t_offset; p = (int)(idx % R::PT);
   } else if (idx < (long)T * R::PT + (long)H * R::PY) {
     const long r = idx - (long)T * R::PT;
-    pos = r / R::PY; i = r % R::PY; da = 3 * D / 8;
+    pos = r / R::PY; p = R::PT + (int)(r % R::PY);
   } else {
     const long r = idx - (long)T * R::PT - (long)H * R::PY;
-    pos = r / R::PX; i = r % R::PX; da = 3 * D / 8;
+    pos = r / R::PX; p = R::PT + R::PY + (int)(r % R::PX);
   }
-  const double ang = (double)pos * pow(10000.0, -2.0 * (double)i / (double)da);
-  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+  tab[idx] = R::cos_sin((double)pos * R::freq_of(p));
 }
 
 // ===========================================================================
