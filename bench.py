@@ -27,8 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}   # dense MFMA of the operand type the kernels use
-# (fp8 I/O is widened to bf16 operands; fp32 I/O runs fp32 MFMA)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "e5m2": 2500.0, "f32": 157.3}   # dense MFMA of the operand type
+# the kernels use (fp8 I/O of either format is widened to bf16 operands; fp32 I/O runs fp32 MFMA)
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
 KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
                   ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
@@ -314,7 +314,7 @@ def cpu_baseline(w, inp, heads_sample: int):
     import oracle.gla_oracle as orc
     from workloads import head_slice_f32
     heads = list(range(min(heads_sample, w.heads)))
-    sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
+    sub = head_slice_f32(inp, heads) if w.dtype != "f32" else {
         **inp, **{n: inp[n][:, heads] for n in ("q", "k", "v", "g", "beta")}}
     if w.block_frames is not None:
         run = lambda: orc.gla_block_causal_forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"],  # noqa: E731
@@ -346,7 +346,7 @@ def cpu_baseline_token_causal(w, inp, include_self: bool, heads_sample: int = 2,
     frames = max(1, min(w.T, round(target_tokens / hw)))
     n = frames * hw
     heads = list(range(min(heads_sample, w.heads)))
-    sub = head_slice_f32(inp, heads) if w.dtype in ("bf16", "fp8") else {
+    sub = head_slice_f32(inp, heads) if w.dtype != "f32" else {
         **inp, **{k: inp[k][:, heads] for k in ("q", "k", "v", "g", "beta")}}
     part = {k: sub[k][:n] for k in ("q", "k", "v", "g", "beta")}
     dt, cores, blas = timed_oracle(
@@ -373,9 +373,9 @@ def main(argv=None):
     # ~3% slower at 720p/60s, 20 or more time the same
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="720p_60s")
-    ap.add_argument("--dtype", choices=("bf16", "fp8", "f32"), default=None,
+    ap.add_argument("--dtype", choices=("bf16", "fp8", "e5m2", "f32"), default=None,
                     help="operator I/O dtype (default: the workload's own, bf16 for 720p_60s); "
-                         "fp8 = OCP FP8 E4M3 q, k, v, g, beta and out")
+                         "fp8 = OCP FP8 E4M3 q, k, v, g, beta and out; e5m2 = OCP FP8 E5M2")
     ap.add_argument("--form", choices=("workload", "token-causal", "token-causal-strict"), default="workload",
                     help="operator form: the workload's own (bidirectional or block-causal), or the token-level "
                          "causal form with the own token included (token-causal) or excluded (-strict)")
@@ -453,8 +453,9 @@ def main(argv=None):
     def upload_one(it, name):
         if w.dtype == "bf16":
             return torch.from_numpy(it[name + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-        if w.dtype == "fp8":
-            return torch.from_numpy(it[name + "_bits"]).to(dev).view(torch.float8_e4m3fn)
+        if w.dtype in ("fp8", "e5m2"):
+            tdt = torch.float8_e4m3fn if w.dtype == "fp8" else torch.float8_e5m2
+            return torch.from_numpy(it[name + "_bits"]).to(dev).view(tdt)
         return torch.from_numpy(it[name]).to(dev)
 
     def upload(name):
@@ -574,7 +575,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "fp8_e4m3"}.get(w.dtype, w.dtype),
+        "dtype": {"fp8": "fp8_e4m3", "e5m2": "fp8_e5m2"}.get(w.dtype, w.dtype),
         "data": "synthetic (seeded N(0,1) q,k,v,g; beta=sigmoid(N(0,1)); rms_w=1+0.1N(0,1))",
         "config": {
             "workload": w.name,

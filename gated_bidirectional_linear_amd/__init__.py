@@ -11,7 +11,8 @@ PyTorch provides device memory and streams.
     out = token_causal_forward(q, k, v, beta, g, rms_w, (T, H, W), state_S, state_z,
                                include_self=True, eps=1e-6)
 
-q, k, v, g: [N, heads, d] (float32, bfloat16 or float8_e4m3fn, contiguous, on the GPU),
+q, k, v, g: [N, heads, d] (float32, bfloat16, float8_e4m3fn or float8_e5m2,
+contiguous, on the GPU),
 beta: [N, heads] same dtype, rms_w: [d] float32, N = T*H*W, d in {32, 64, 128}.
 A leading batch dimension ([B, N, heads, d], beta [B, N, heads], states
 [B, heads, d, d] and [B, heads, d]) runs B independent sequences of the same
@@ -43,11 +44,13 @@ __all__ = [
     "DTYPE_F32",
     "DTYPE_BF16",
     "DTYPE_FP8_E4M3",
+    "DTYPE_FP8_E5M2",
 ]
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
+DTYPE_FP8_E5M2 = 3
 NUM_KERNELS = 4
 
 
@@ -78,7 +81,9 @@ def _dtype_code(t) -> int:
         return DTYPE_BF16
     if t.dtype == torch.float8_e4m3fn:
         return DTYPE_FP8_E4M3
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float8_e4m3fn")
+    if t.dtype == torch.float8_e5m2:
+        return DTYPE_FP8_E5M2
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16, float8_e4m3fn or float8_e5m2")
 
 
 def _check(name, t, shape, dtype, device):

@@ -260,6 +260,11 @@ void prepare_pool() {
 // ---------------------------------------------------------------------------
 // validation
 // ---------------------------------------------------------------------------
+// bytes per element of an I/O dtype (a known one)
+int elem_size(int dtype) {
+  return dtype == GLA_DTYPE_BF16 ? 2 : ((dtype == GLA_DTYPE_FP8_E4M3 || dtype == GLA_DTYPE_FP8_E5M2) ? 1 : 4);
+}
+
 struct Range { uintptr_t lo, hi; };
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -274,7 +279,8 @@ Range range_of(const void* p, size_t bytes) {
 int validate(const void* q, const void* k, const void* v, const void* beta, const void* g, const float* rms_w,
              int T, int H, int W, int heads, int d, float eps, const void* out, int dtype, bool causal,
              const float* S, const float* z, int block_frames, int batch) {
-  if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16 && dtype != GLA_DTYPE_FP8_E4M3) return GLA_ERR_DTYPE;
+  if (dtype != GLA_DTYPE_F32 && dtype != GLA_DTYPE_BF16 && dtype != GLA_DTYPE_FP8_E4M3 && dtype != GLA_DTYPE_FP8_E5M2)
+    return GLA_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return GLA_ERR_UNSUPPORTED_D;
   if (T < 0 || H < 0 || W < 0 || heads < 1 || batch < 1) return GLA_ERR_SHAPE;
   if (!(std::isfinite(eps) && eps >= FLT_MIN)) return GLA_ERR_SHAPE;
@@ -291,7 +297,7 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
   if (N * heads * d >= (1LL << 40)) return GLA_ERR_SHAPE;
   // the kernels address up to 64 token rows of all heads through one 32-bit
   // buffer range: a token row (heads * d elements) must stay below 2^26 bytes
-  const long long es_row = dtype == GLA_DTYPE_BF16 ? 2 : (dtype == GLA_DTYPE_FP8_E4M3 ? 1 : 4);
+  const long long es_row = elem_size(dtype);
   if ((long long)heads * d * es_row >= (1LL << 26)) return GLA_ERR_SHAPE;
   if (N == 0) return GLA_OK;  // nothing is read or written
   const void* ptrs[] = {q, k, v, beta, g, rms_w, out, causal ? S : rms_w, causal ? z : rms_w};
@@ -299,7 +305,7 @@ int validate(const void* q, const void* k, const void* v, const void* beta, cons
     if (p == nullptr) return GLA_ERR_NULL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return GLA_ERR_ALIGN;
-  const size_t es = dtype == GLA_DTYPE_BF16 ? 2 : (dtype == GLA_DTYPE_FP8_E4M3 ? 1 : 4);
+  const size_t es = (size_t)elem_size(dtype);
   const size_t big = (size_t)N * heads * d * es;
   const Range rin[] = {range_of(q, big), range_of(k, big), range_of(v, big), range_of(g, big),
                        range_of(beta, (size_t)N * heads * es), range_of(rms_w, (size_t)d * 4)};
@@ -331,7 +337,7 @@ int run(Form form, const void* q, const void* k, const void* v, const void* beta
   const Knobs kn = Knobs::snapshot();
   const int seg_len = segment_length(form, T, H, W, heads, block_frames, batch, kn);
   Geometry G = plan(T, H, W, heads, d, eps, seg_len, form == Form::token_causal,
-                    dtype == GLA_DTYPE_BF16 || dtype == GLA_DTYPE_FP8_E4M3, dtype == GLA_DTYPE_BF16, batch, kn);
+                    elem_size(dtype) <= 2, dtype == GLA_DTYPE_BF16, batch, kn);
   G.t_offset = t_offset;
   G.include_self = include_self;
   const size_t rope_bytes =

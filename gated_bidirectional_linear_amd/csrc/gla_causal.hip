@@ -98,11 +98,15 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* X, int pitch, int tok0, 
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// The 8 channels of a raw row as 4 bf16 pairs (fp8 widens exactly).
-__device__ __forceinline__ u32x4 bf16_words(const u32x4& r) { return r; }
-__device__ __forceinline__ u32x4 bf16_words(const u32x2& r) {
-  return (u32x4){Elem<fp8_t>::bf16_pair<false>(r.x), Elem<fp8_t>::bf16_pair<true>(r.x),
-                 Elem<fp8_t>::bf16_pair<false>(r.y), Elem<fp8_t>::bf16_pair<true>(r.y)};
+// The 8 channels of a raw row as 4 bf16 pairs (fp8 of either format widens exactly).
+template <typename E>
+__device__ __forceinline__ u32x4 bf16_words(const typename Elem<E>::Raw& r) {
+  if constexpr (Elem<E>::is_f8) {
+    return (u32x4){Elem<E>::template bf16_pair<false>(r.x), Elem<E>::template bf16_pair<true>(r.x),
+                   Elem<E>::template bf16_pair<false>(r.y), Elem<E>::template bf16_pair<true>(r.y)};
+  } else {
+    return r;
+  }
 }
 
 // LDS copy of the RoPE rows a segment needs (frames [t_lo, t_lo + nt), then
@@ -176,6 +180,13 @@ template <> struct BetaLoad<bf16_t> {
     return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
   }
   __device__ __forceinline__ static float value(Raw x) { return __uint_as_float((uint32_t)x << 16); }
+};
+template <> struct BetaLoad<bf8_t> {
+  typedef unsigned char Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (unsigned char)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static float value(Raw x) { return __builtin_amdgcn_cvt_f32_bf8((int)x, 0); }
 };
 template <> struct BetaLoad<fp8_t> {
   typedef unsigned char Raw;
@@ -393,7 +404,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
               wb[j] = pack2bf(cs[i].s[j], cs[i].c[j]);
             }
           }
-          const u32x4 qw = bf16_words(qr[i]), kw = bf16_words(kr[i]);
+          const u32x4 qw = bf16_words<E>(qr[i]), kw = bf16_words<E>(kr[i]);
           float ssq = dot2bf(qw.x, qw.x, dot2bf(qw.y, qw.y, dot2bf(qw.z, qw.z, dot2bf(qw.w, qw.w, 0.f))));
           float ssk = dot2bf(kw.x, kw.x, dot2bf(kw.y, kw.y, dot2bf(kw.z, kw.z, dot2bf(kw.w, kw.w, 0.f))));
           ssq = group_sum<C::CG>(ssq);
@@ -431,7 +442,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
           }
           *reinterpret_cast<u32x4*>(rqs(hl) + tok * C::RP + 8 * cg) = Elem<bf16_t>::pack(rq);
           *reinterpret_cast<u32x4*>(rks(hl) + tok * C::RPK + 8 * cg) = Elem<bf16_t>::pack(rk);
-          *reinterpret_cast<u32x4*>(vT(hl) + tok * C::RPV + 8 * cg) = bf16_words(vr[i]);
+          *reinterpret_cast<u32x4*>(vT(hl) + tok * C::RPV + 8 * cg) = bf16_words<E>(vr[i]);
         }
       } else {
         // fp32 operands: fp32 features and transposed LDS copies of rk and v
@@ -710,5 +721,8 @@ template hipError_t launch_token_causal<128, bf16_t>(const LaunchArgs&);
 template hipError_t launch_token_causal<32, fp8_t>(const LaunchArgs&);
 template hipError_t launch_token_causal<64, fp8_t>(const LaunchArgs&);
 template hipError_t launch_token_causal<128, fp8_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<32, bf8_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<64, bf8_t>(const LaunchArgs&);
+template hipError_t launch_token_causal<128, bf8_t>(const LaunchArgs&);
 
 }  // namespace gla

@@ -13,6 +13,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short bf16_t;  // bf16 storage
 typedef unsigned char fp8_t;    // OCP FP8 E4M3 (e4m3fn) storage
+enum class bf8_t : unsigned char {};   // OCP FP8 E5M2 storage (a distinct one-byte type)
 
 constexpr int kTile = 64;       // tokens per staged tile
 constexpr int kThreads = 256;   // 4 waves of 64
@@ -38,6 +39,7 @@ template <typename E> struct Elem;
 
 template <> struct Elem<float> {
   static constexpr bool is_bf16 = false;
+  static constexpr bool is_f8 = false;
   typedef float Lds;   // LDS staging / MFMA operand type
   struct Raw { f32x4 a, b; };  // 8 channels as loaded
   __device__ __forceinline__ static Raw load_raw(const float* p) {
@@ -75,6 +77,7 @@ template <> struct Elem<float> {
 
 template <> struct Elem<bf16_t> {
   static constexpr bool is_bf16 = true;
+  static constexpr bool is_f8 = false;
   typedef bf16_t Lds;
   typedef u32x4 Raw;  // 8 channels as loaded
   __device__ __forceinline__ static Raw load_raw(const bf16_t* p) {
@@ -111,6 +114,7 @@ template <> struct Elem<bf16_t> {
 // kernels stage fp8 operands as bf16 for the MFMA.
 template <> struct Elem<fp8_t> {
   static constexpr bool is_bf16 = false;
+  static constexpr bool is_f8 = true;
   typedef bf16_t Lds;
   typedef u32x2 Raw;  // 8 channels as loaded
   __device__ __forceinline__ static Raw load_raw(const fp8_t* p) {
@@ -142,6 +146,49 @@ template <> struct Elem<fp8_t> {
   __device__ __forceinline__ static uint32_t bf16_pair(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, SEL));
   }
+  __device__ __forceinline__ static float code_to_f32(int code) { return __builtin_amdgcn_cvt_f32_fp8(code, 0); }
+};
+
+// FP8 E5M2 (OCP: bias 15, max 57344, with infinities and NaN).  gfx950's
+// v_cvt_pk_f32_bf8 / v_cvt_pk_bf8_f32 convert it, rounding to nearest even;
+// every e5m2 value is exact in bf16 (and in fp32), so the kernels treat it as
+// the e4m3 rows above with the other conversion instructions.
+template <> struct Elem<bf8_t> {
+  static constexpr bool is_bf16 = false;
+  static constexpr bool is_f8 = true;
+  typedef bf16_t Lds;
+  typedef u32x2 Raw;  // 8 channels as loaded
+  __device__ __forceinline__ static Raw load_raw(const bf8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  __device__ __forceinline__ static void unpack(const Raw& u, float (&x)[8]) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v a = __builtin_amdgcn_cvt_pk_f32_bf8((int)u.x, false), b = __builtin_amdgcn_cvt_pk_f32_bf8((int)u.x, true);
+    const f2v c = __builtin_amdgcn_cvt_pk_f32_bf8((int)u.y, false), d = __builtin_amdgcn_cvt_pk_f32_bf8((int)u.y, true);
+    x[0] = a.x; x[1] = a.y; x[2] = b.x; x[3] = b.y; x[4] = c.x; x[5] = c.y; x[6] = d.x; x[7] = d.y;
+  }
+  __device__ __forceinline__ static void load8(const bf8_t* p, float (&x)[8]) { unpack(load_raw(p), x); }
+  __device__ __forceinline__ static Raw pack(const float (&x)[8]) {
+    int w0 = __builtin_amdgcn_cvt_pk_bf8_f32(x[0], x[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_bf8_f32(x[2], x[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_bf8_f32(x[4], x[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_bf8_f32(x[6], x[7], w1, true);
+    return (u32x2){(uint32_t)w0, (uint32_t)w1};
+  }
+  __device__ __forceinline__ static void store8(bf8_t* p, const float (&x)[8]) {
+    __builtin_nontemporal_store(pack(x), reinterpret_cast<u32x2*>(p));
+  }
+  __device__ __forceinline__ static void store_raw(bf8_t* p, const Raw& r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x2*>(p));
+  }
+  __device__ __forceinline__ static float load1(const bf8_t* p) {
+    return __builtin_amdgcn_cvt_f32_bf8((int)static_cast<unsigned char>(*p), 0);
+  }
+  template <bool SEL>
+  __device__ __forceinline__ static uint32_t bf16_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w, 1.0f, SEL));
+  }
+  __device__ __forceinline__ static float code_to_f32(int code) { return __builtin_amdgcn_cvt_f32_bf8(code, 0); }
 };
 
 // ---------------------------------------------------------------------------
@@ -411,6 +458,16 @@ template <> struct BufRow<bf16_t> {
     buf_store16(r, voff, soff, v);
   }
 };
+template <typename E> struct BufRow8 {   // 8 channels of one-byte elements: 8 bytes
+  typedef u32x2 Raw;
+  __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadStream));
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const Raw& v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, kStoreStream);
+  }
+};
+template <> struct BufRow<bf8_t> : BufRow8<bf8_t> {};
 template <> struct BufRow<fp8_t> {
   typedef u32x2 Raw;
   __device__ __forceinline__ static Raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -442,12 +499,14 @@ __device__ __forceinline__ float dot2sq(uint32_t u, float acc) {
   const bf16x2 v = __builtin_bit_cast(bf16x2, u);
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
-// Gates read as fp8 e4m3 take sigmoid(g) from a table of all 256 codes in
-// LDS: one read per element in place of a decode, an exp and a reciprocal.
-// The entries use the per-element formula, so the results are the same.
+// Gates read as fp8 (e4m3 or e5m2) take sigmoid(g) from a table of all 256
+// codes in LDS: one read per element in place of a decode, an exp and a
+// reciprocal.  The entries use the per-element formula, so the results are the
+// same.
+template <typename E>
 __device__ __forceinline__ void fill_sigmoid_fp8(float* tab, int tid, int nthreads) {
   for (int i = tid; i < 256; i += nthreads)
-    tab[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-__builtin_amdgcn_cvt_f32_fp8(i, 0)));
+    tab[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-Elem<E>::code_to_f32(i)));
 }
 // sigmoid of code `byte` (0..3) of the packed word w
 __device__ __forceinline__ float sigmoid_fp8(const float* tab, uint32_t w, int byte) {

@@ -8,6 +8,7 @@ namespace gla {
 
 typedef unsigned short bf16_t;
 typedef unsigned char fp8_t;
+enum class bf8_t : unsigned char {};
 
 template <int D> hipError_t launch_rope_table(const LaunchArgs& a);
 template <int D> hipError_t launch_state_reduce(const LaunchArgs& a);
@@ -39,7 +40,7 @@ static hipError_t launch_all(const LaunchArgs& a, Timer& tm) {
 }
 
 hipError_t launch_operator(const LaunchArgs& a, Timer& tm) {
-  // dtype codes of include/gla.h: 0 fp32, 1 bf16, 2 fp8 e4m3
+  // dtype codes of include/gla.h: 0 fp32, 1 bf16, 2 fp8 e4m3, 3 fp8 e5m2
   if (a.dtype == 1) {
     switch (a.geo.d) {
       case 32: return launch_all<32, bf16_t>(a, tm);
@@ -51,6 +52,12 @@ hipError_t launch_operator(const LaunchArgs& a, Timer& tm) {
       case 32: return launch_all<32, fp8_t>(a, tm);
       case 64: return launch_all<64, fp8_t>(a, tm);
       case 128: return launch_all<128, fp8_t>(a, tm);
+    }
+  } else if (a.dtype == 3) {
+    switch (a.geo.d) {
+      case 32: return launch_all<32, bf8_t>(a, tm);
+      case 64: return launch_all<64, bf8_t>(a, tm);
+      case 128: return launch_all<128, bf8_t>(a, tm);
     }
   } else if (a.dtype == 0) {
     switch (a.geo.d) {

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   constexpr int SZ = D * D + D;
   constexpr int ROPE_BYTES = LDSR ? kRopeLdsEntries * 8 : 0;
   constexpr bool kBf16 = Elem<E>::is_bf16;
-  constexpr bool kFp8 = sizeof(E) == 1;
+  constexpr bool kFp8 = Elem<E>::is_f8;
   constexpr int SIG_BYTES = kFp8 ? 256 * 4 : 0;   // sigmoid of every fp8 gate code
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM + ROPE_BYTES + SIG_BYTES];
   constexpr int kT = C::TILE;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(
   const int hi = lane >> 5;
   // read first in a tile's epilogue, after that tile's two barriers
   float* sig_tab = reinterpret_cast<float*>(smem + C::SMEM + ROPE_BYTES);
-  if constexpr (kFp8) fill_sigmoid_fp8(sig_tab, tid, kThreads);
+  if constexpr (kFp8) fill_sigmoid_fp8<E>(sig_tab, tid, kThreads);
 
   // Every tile's loads and stores go through buffer resources based at the
   // tile's first row and this head and ending at the chunk's last row: rows
@@ -727,9 +727,9 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
       pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
       u32x4 u;   // 8 channels as bf16 pairs (fp8 widens exactly)
-      if constexpr (sizeof(E) == 1) {
-        u = (u32x4){Elem<fp8_t>::bf16_pair<false>(qt[i].x), Elem<fp8_t>::bf16_pair<true>(qt[i].x),
-                    Elem<fp8_t>::bf16_pair<false>(qt[i].y), Elem<fp8_t>::bf16_pair<true>(qt[i].y)};
+      if constexpr (Elem<E>::is_f8) {
+        u = (u32x4){Elem<E>::template bf16_pair<false>(qt[i].x), Elem<E>::template bf16_pair<true>(qt[i].x),
+                    Elem<E>::template bf16_pair<false>(qt[i].y), Elem<E>::template bf16_pair<true>(qt[i].y)};
       } else {
         u = qt[i];
       }
@@ -845,5 +845,8 @@ template hipError_t launch_output<128, bf16_t>(const LaunchArgs&);
 template hipError_t launch_output<32, fp8_t>(const LaunchArgs&);
 template hipError_t launch_output<64, fp8_t>(const LaunchArgs&);
 template hipError_t launch_output<128, fp8_t>(const LaunchArgs&);
+template hipError_t launch_output<32, bf8_t>(const LaunchArgs&);
+template hipError_t launch_output<64, bf8_t>(const LaunchArgs&);
+template hipError_t launch_output<128, bf8_t>(const LaunchArgs&);
 
 }  // namespace gla

@@ -270,6 +270,22 @@ template <> struct Io<bf16_t> {
   }
   __device__ __forceinline__ static int beta_f32_bits(uint32_t b) { return (int)(b << 16); }
 };
+template <> struct Io<bf8_t> {
+  static constexpr uint32_t ES = 1;
+  typedef uint32_t Word;
+  __device__ __forceinline__ static Word load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, kLoadStream);
+  }
+  __device__ __forceinline__ static u32x2 bf16x4(Word w) {
+    return (u32x2){Elem<bf8_t>::bf16_pair<false>(w), Elem<bf8_t>::bf16_pair<true>(w)};
+  }
+  __device__ __forceinline__ static uint32_t load_beta(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ static int beta_f32_bits(uint32_t b) {
+    return __float_as_int(__builtin_amdgcn_cvt_f32_bf8((int)b, 0));
+  }
+};
 template <> struct Io<fp8_t> {
   static constexpr uint32_t ES = 1;
   typedef uint32_t Word;
@@ -627,5 +643,8 @@ template hipError_t launch_state_partial<128, bf16_t>(const LaunchArgs&);
 template hipError_t launch_state_partial<32, fp8_t>(const LaunchArgs&);
 template hipError_t launch_state_partial<64, fp8_t>(const LaunchArgs&);
 template hipError_t launch_state_partial<128, fp8_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<32, bf8_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<64, bf8_t>(const LaunchArgs&);
+template hipError_t launch_state_partial<128, bf8_t>(const LaunchArgs&);
 
 }  // namespace gla

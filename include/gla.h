@@ -76,12 +76,18 @@ typedef enum {
 typedef enum {
   GLA_DTYPE_F32 = 0,      /* q, k, v, g, beta, out are float32 */
   GLA_DTYPE_BF16 = 1,     /* q, k, v, g, beta, out are bfloat16 (fp32 accumulation inside) */
-  GLA_DTYPE_FP8_E4M3 = 2  /* q, k, v, g, beta, out are OCP FP8 E4M3 (e4m3fn: bias 7, max 448,
+  GLA_DTYPE_FP8_E4M3 = 2, /* q, k, v, g, beta, out are OCP FP8 E4M3 (e4m3fn: bias 7, max 448,
                              no infinities), one byte each; the state, the denominators and all
                              accumulation stay fp32 and the output is rounded to nearest even.
                              Low-precision operator I/O halves the bytes of a bandwidth-bound
                              op (SANA-Video 2.0 digest, weaknesses: the attention operator stays
                              BF16, so quantisation of the linear GEMMs alone saves only 5.8%). */
+  GLA_DTYPE_FP8_E5M2 = 3  /* q, k, v, g, beta, out are OCP FP8 E5M2 (bias 15, max 57344, with
+                             infinities and NaN; inputs must be finite), one byte each;
+                             otherwise as GLA_DTYPE_FP8_E4M3:
+                             fp32 state, denominators and accumulation, output rounded to nearest
+                             even.  It trades one mantissa bit (2 against 3) for a range of 2^-16 to
+                             57344, for inputs whose scale varies more than e4m3 holds. */
 } gla_dtype;
 
 /*

@@ -94,7 +94,7 @@ int main() {
   for (Entry e : kAll) {
     Args a;
     // dtype and head dim
-    for (int dt : {-1, 3, 7}) { a = Args(); a.dtype = dt; EXPECT(e(a), GLA_ERR_DTYPE); }
+    for (int dt : {-1, 4, 7}) { a = Args(); a.dtype = dt; EXPECT(e(a), GLA_ERR_DTYPE); }
     for (int d : {0, 16, 48, 96, 256}) { a = Args(); a.d = d; EXPECT(e(a), GLA_ERR_UNSUPPORTED_D); }
     // shapes, eps and size limits
     a = Args(); a.T = -1; EXPECT(e(a), GLA_ERR_SHAPE);

@@ -112,9 +112,9 @@ def test_frame_offset_errors(lib):
 
 
 def test_dtype_and_head_dim_errors(lib):
-    assert fwd(lib, dtype=3) == E_DTYPE          # 0 fp32, 1 bf16, 2 fp8 e4m3 are the known codes
+    assert fwd(lib, dtype=4) == E_DTYPE          # 0 fp32, 1 bf16, 2 fp8 e4m3, 3 fp8 e5m2 are the known codes
     assert fwd(lib, dtype=-1) == E_DTYPE
-    for dt in (0, 1, 2):                          # known dtypes reach the later checks
+    for dt in (0, 1, 2, 3):                       # known dtypes reach the later checks
         assert fwd(lib, dtype=dt, d=48) == E_D
         assert fwd(lib, dtype=dt, heads=0) == E_SHAPE
     for d in (0, 16, 48, 96, 256):
@@ -298,7 +298,7 @@ def fna(lib, T=2, H=4, W=4, heads=2, d=32, eps=1e-6, dtype=1, ptrs=None):
 def test_noalloc_validation_and_size_limit(lib):
     """gla_forward_noalloc validates like gla_forward and rejects, before any
     device work, calls whose scratch exceeds its 64 MiB static buffer."""
-    assert fna(lib, dtype=3) == E_DTYPE
+    assert fna(lib, dtype=4) == E_DTYPE
     assert fna(lib, d=48) == E_D
     assert fna(lib, heads=0) == E_SHAPE
     assert fna(lib, ptrs=[None] + P[1:]) == E_NULL

@@ -12,7 +12,7 @@ from tests.gpu_helpers import (TOL, Z_TOL, fp8_excess, rel_err, run_block_causal
 
 pytestmark = pytest.mark.gpu
 
-S_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+S_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2, "e5m2": 1e-2}
 
 
 def _items(B, T, H, W, heads, d, dtype, seed, eps=1e-6):
@@ -31,7 +31,7 @@ def _stack(its):
 
 
 def _err(got, ref, dtype):
-    return fp8_excess(got, ref) if dtype == "fp8" else rel_err(got, ref)
+    return fp8_excess(got, ref, dtype) if dtype in ("fp8", "e5m2") else rel_err(got, ref)
 
 
 def _oracle(it, **kw):
@@ -44,6 +44,7 @@ SHAPES = [
     (3, 4, 6, 10, 4, 128, "bf16"),
     (2, 5, 9, 3, 3, 128, "bf16"),
     (3, 3, 4, 5, 2, 128, "fp8"),
+    (2, 3, 4, 5, 4, 128, "e5m2"),
 ]
 
 

@@ -17,7 +17,7 @@ from tests.gpu_helpers import (TOL, Z_TOL, to_device, to_f64, rel_err, fp8_exces
 
 pytestmark = pytest.mark.gpu
 
-S_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2}
+S_TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 1e-2, "e5m2": 1e-2}
 
 
 def _oracle_tc(inp, include_self, S0=None, z0=None, **kw):
@@ -26,7 +26,7 @@ def _oracle_tc(inp, include_self, S0=None, z0=None, **kw):
 
 
 def _out_err(got, ref, dtype):
-    return fp8_excess(got, ref) if dtype == "fp8" else rel_err(got, ref)
+    return fp8_excess(got, ref, dtype) if dtype in ("fp8", "e5m2") else rel_err(got, ref)
 
 
 def _check(name, inp, include_self, S0=None, z0=None, t_offset=0):
@@ -54,6 +54,8 @@ SHAPES = [
     (3, 4, 6, 3, 128, "bf16"),   # odd head count: one head per workgroup
     (3, 4, 5, 2, 128, "fp8"),
     (2, 5, 9, 2, 64, "fp8"),
+    (3, 4, 5, 2, 128, "e5m2"),
+    (2, 5, 9, 3, 64, "e5m2"),
 ]
 
 
@@ -230,7 +232,7 @@ def test_token_causal_long_sequence_sampled(include_self, dtype):
         return orc.gla_token_causal_rows(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], sub["rms_w"],
                                          sub["grid"], sub["eps"], rows, include_self=include_self)
 
-    err = grouped_head_error(out, inp, ref_rows, kind="fp8" if dtype == "fp8" else "rel", rows=rows,
+    err = grouped_head_error(out, inp, ref_rows, kind=dtype if dtype in ("fp8", "e5m2") else "rel", rows=rows,
                              label=f"tc 720p_60s {dtype} incl={include_self}")
     print(f"[parity] tc 720p_60s {dtype} all heads, {len(rows)} rows, incl={include_self}: error {err:.3e}",
           flush=True)

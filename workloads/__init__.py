@@ -3,7 +3,7 @@
 This module is shared by the tests, the benchmark and the smoke check. It holds
 only input construction: the workload table (grid, heads, head dim, dtype,
 block size), seeded random draws, and the storage conversion of fp32 draws to
-bfloat16 bits. None of the operator's arithmetic lives here.
+bfloat16 and fp8 bits. None of the operator's arithmetic lives here.
 
 Workload shapes follow the pages' video-latent grids (SANA-Video 2.0 digest,
 "results" table and the 480p/720p workloads; SANA-Video notes, block linear
@@ -14,7 +14,8 @@ Draw recipe: q, k, v, g ~ N(0,1) fp32, beta = sigmoid(N(0,1)), rms_w =
 1 + 0.1*N(0,1) fp32, every tensor from its own counter-keyed PCG64 streams
 (see make_inputs).  For bf16 workloads every tensor handed to the operator
 (q, k, v, g, beta) is rounded to bfloat16 with round-to-nearest-even; rms_w
-stays fp32.
+stays fp32.  fp8 (OCP E4M3) and e5m2 (OCP E5M2) workloads round the same
+tensors to their format the same way.
 """
 from __future__ import annotations
 
@@ -34,6 +35,10 @@ __all__ = [
     "fp8_bits_to_f32",
     "round_to_fp8",
     "FP8_MAX",
+    "f32_to_e5m2_bits",
+    "e5m2_bits_to_f32",
+    "round_to_e5m2",
+    "E5M2_MAX",
 ]
 
 
@@ -45,7 +50,7 @@ class Workload:
     W: int
     heads: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16", "fp8" (OCP E4M3) or "e5m2" (OCP E5M2)
     block_frames: Optional[int] = None  # None: bidirectional
     eps: float = 1e-6
 
@@ -55,7 +60,7 @@ class Workload:
 
     @property
     def elem_size(self) -> int:
-        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+        return {"f32": 4, "bf16": 2, "fp8": 1, "e5m2": 1}[self.dtype]
 
     def alg_bytes(self) -> int:
         """Algorithmic HBM bytes of one call: read q,k,v,g,beta, write out,
@@ -150,6 +155,54 @@ def round_to_fp8(x: np.ndarray) -> np.ndarray:
     return fp8_bits_to_f32(f32_to_fp8_bits(x))
 
 
+# OCP FP8 E5M2: sign, 5 exponent bits (bias 15), 2 mantissa bits; exponent
+# field 0 holds subnormals m * 2^-16; exponent field 31 holds +-infinity
+# (mantissa 0) and NaN; the largest finite value is 57344 (S.11110.11).
+E5M2_MAX = 57344.0
+
+
+def e5m2_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Decode FP8 E5M2 bits (uint8) to fp32 values."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int32)
+    e = (b >> 2) & 0x1F
+    m = b & 3
+    mag = np.where(e == 0, m * 2.0 ** -16, (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
+
+
+def f32_to_e5m2_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite values to FP8 E5M2, nearest with ties to even, saturating
+    magnitudes past 57344 to 57344; returns uint8 bits.  Inputs must be finite."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int32)
+    # subnormal range (a < 2^-14): units of 2^-16; 4 units is the smallest normal (code 4)
+    sub = np.rint(a * 2.0 ** 16).astype(np.int64)
+    f, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = ex.astype(np.int64) - 1
+    q = np.rint((2.0 * f - 1.0) * 4.0).astype(np.int64)   # 0..4 quarters above 1
+    e = np.where(q == 4, e + 1, e)
+    q = np.where(q == 4, 0, q)
+    norm = (np.clip(e + 15, 0, 31) << 2) | q
+    code = np.where(a < 2.0 ** -14, sub, norm)
+    code = np.where(a >= E5M2_MAX, 0x7B, np.minimum(code, 0x7B))
+    return (code.astype(np.int32) | sign).astype(np.uint8)
+
+
+def round_to_e5m2(x: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest FP8 E5M2 value, returned as fp32."""
+    return e5m2_bits_to_f32(f32_to_e5m2_bits(x))
+
+
+# storage codecs of the narrow dtypes: (numpy storage type, encode, decode)
+CODECS = {
+    "bf16": (np.uint16, f32_to_bf16_bits, bf16_bits_to_f32),
+    "fp8": (np.uint8, f32_to_fp8_bits, fp8_bits_to_f32),
+    "e5m2": (np.uint8, f32_to_e5m2_bits, e5m2_bits_to_f32),
+}
+
+
 _BLOCK = 1 << 22          # elements per independently seeded block
 _STREAMS = {"q": 0, "k": 1, "v": 2, "g": 3, "beta": 4, "rms_w": 5}
 
@@ -168,11 +221,16 @@ def _workers() -> int:
     return max(1, min(16, n))
 
 
+def _codec(dtype: str):
+    """(encode, decode) of a narrow storage dtype."""
+    return CODECS[dtype][1], CODECS[dtype][2]
+
+
 def _draw(seed: int, name: str, shape, dtype: str, keep_f32: bool, pool, sigmoid: bool = False):
     size = int(np.prod(shape))
     f32 = np.empty(size, np.float32) if (keep_f32 or dtype == "f32") else None
-    bits = np.empty(size, {"bf16": np.uint16, "fp8": np.uint8}[dtype]) if dtype != "f32" else None
-    encode, decode = (f32_to_fp8_bits, fp8_bits_to_f32) if dtype == "fp8" else (f32_to_bf16_bits, bf16_bits_to_f32)
+    bits = np.empty(size, CODECS[dtype][0]) if dtype != "f32" else None
+    encode, decode = _codec(dtype) if dtype != "f32" else (None, None)
     stream = _STREAMS[name]
 
     def work(b):
@@ -204,17 +262,17 @@ def make_inputs(T: int, H: int, W: int, heads: int, d: int, dtype: str, seed: in
 
     Returns a dict with fp32 numpy arrays ``q, k, v, g`` of shape [N, heads, d],
     ``beta`` [N, heads], ``rms_w`` [d], plus ``eps``, ``grid`` (T, H, W) and
-    ``dtype``.  For dtype "bf16" ("fp8") the fp32 arrays hold exactly the bf16
-    (FP8 E4M3) values the operator receives, and ``*_bits`` (uint16, uint8)
-    hold their storage; with keep_f32=False only the bits are kept (large
-    workloads).
+    ``dtype``.  For dtype "bf16" ("fp8", "e5m2") the fp32 arrays hold exactly
+    the bf16 (FP8 E4M3, FP8 E5M2) values the operator receives, and ``*_bits``
+    (uint16, uint8) hold their storage; with keep_f32=False only the bits are
+    kept (large workloads).
 
     Each tensor is filled in row-major order in blocks of 2^22 elements; block
     b of tensor t (q, k, v, g, beta-logit, rms_w-noise = 0..5) is drawn from
     PCG64(SeedSequence(seed, spawn_key=(t, b))), so the values do not depend
     on how many threads draw them.
     """
-    if dtype not in ("f32", "bf16", "fp8"):
+    if dtype not in ("f32", "bf16", "fp8", "e5m2"):
         raise ValueError(f"unknown dtype {dtype!r}")
     N = T * H * W
     from concurrent.futures import ThreadPoolExecutor
@@ -249,7 +307,7 @@ def make_workload_inputs(w: Workload, seed: int = 0, keep_f32: bool = True) -> d
 def head_slice_f32(inp: dict, heads) -> dict:
     """fp32 copies of the listed heads of a bits-only bf16 or fp8 input set."""
     out = dict(inp)
-    decode = fp8_bits_to_f32 if inp["dtype"] == "fp8" else bf16_bits_to_f32
+    decode = _codec(inp["dtype"])[1]
     for name in ("q", "k", "v", "g"):
         out[name] = decode(inp[name + "_bits"][:, heads, :])
     out["beta"] = decode(inp["beta_bits"][:, heads])
