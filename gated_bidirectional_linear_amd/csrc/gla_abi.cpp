@@ -40,10 +40,18 @@ constexpr int kPair2MinTiles = 3;
 constexpr int kPair2LongChunk = 2048;
 // The four-head output kernel (bf16, d = 128, heads divisible by 4) runs one
 // workgroup of 16 waves per CU: its launch aims for one round of 256
-// workgroups, with chunks of at least kQuad2MinTiles tiles (each workgroup
-// first reads its four heads' 128 KB of bf16 state).
+// workgroups, with chunks of whole 64-token tiles, at least kQuad2MinTiles of
+// them (each workgroup first reads its four heads' 128 KB of bf16 state).
+// Where that round would leave more than a quarter of the CUs idle (short
+// sequences), the chunks are cut in the kernel's own 16-token tiles instead,
+// at least kQuad2MinUnits of them.  Measured (whole call): 480p 51.2 us with
+// 225 workgroups of 96 tokens against 52.3-53.8 us with 170 of 128;
+// 720p/5s with 20 heads 93.3 us with 220 workgroups of 320 tokens against
+// 96.6 us with 245 of 288.
 constexpr int kQuad2Slots = 256;
 constexpr int kQuad2MinTiles = 2;
+constexpr int kQuadTile = 16;
+constexpr int kQuad2MinUnits = 6;
 
 // Launch-plan overrides (include/gla_internal.h): process-wide, 0 = the
 // measured default.  Every call reads them once, into a Knobs snapshot, so a
@@ -149,11 +157,19 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     else if (bf16_io && heads % 2 == 0 && max_hp >= 2) G.pass2_pair = 2;
   }
   const int per_seg_units2 = G.pass2_pair ? per_seg_heads / G.pass2_pair : per_seg_heads;
+  // pass-2 chunks come in whole units of unit2 tokens
+  int unit2 = kTile;
   int want2 = ceil_div(kn.get(GLA_PLAN_PASS2_WORKGROUPS, kDefaultTargetWg2), per_seg_units2);
   if (G.pass2_pair == 4 && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
     want2 = kQuad2Slots / per_seg_units2;   // chunks per segment in one round
     const int most = ceil_div(tiles_per_seg, kQuad2MinTiles);
     if (want2 > most) want2 = most;
+    if (4L * per_seg_units2 * (want2 < 1 ? 1 : want2) < 3L * kQuad2Slots) {   // a quarter of the CUs idle
+      unit2 = kQuadTile;
+      want2 = kQuad2Slots / per_seg_units2;
+      const int most_q = ceil_div(G.seg_len, kQuadTile * kQuad2MinUnits);
+      if (want2 > most_q) want2 = most_q;
+    }
   } else if (G.pass2_pair && !kn.on(GLA_PLAN_PASS2_WORKGROUPS)) {
     want2 = kPair2Slots / per_seg_units2;   // chunks per segment in one round
     if (want2 < 1) want2 = 1;
@@ -161,10 +177,11 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     const int most = ceil_div(tiles_per_seg, kPair2MinTiles);
     if (want2 > most) want2 = most;
   }
+  const int units_per_seg2 = ceil_div(G.seg_len, unit2);
   int cps2 = want2 < 1 ? 1 : want2;
-  if (cps2 > tiles_per_seg) cps2 = tiles_per_seg;
-  while (!rope_fits((long)ceil_div(tiles_per_seg, cps2) * kTile) && cps2 < tiles_per_seg) ++cps2;
-  G.chunk2 = ceil_div(tiles_per_seg, cps2) * kTile;
+  if (cps2 > units_per_seg2) cps2 = units_per_seg2;
+  while (!rope_fits((long)ceil_div(units_per_seg2, cps2) * unit2) && cps2 < units_per_seg2) ++cps2;
+  G.chunk2 = ceil_div(units_per_seg2, cps2) * unit2;
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
   if (token_causal) {   // one workgroup walks a whole segment (of one head, or of a head pair)

@@ -40,9 +40,11 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 //    exclusive (the token-causal form, whose segments are walked token by
 //    token).  One thread per (state element, head, item).  When sbf is given,
 //    each segment's S is also written rounded to bf16 (the operand the
-//    four-head output kernel loads as MFMA fragments).
+//    four-head output kernel loads as MFMA fragments).  P: the chunk count
+//    rounded up to a power of two (1: one partial per segment), so that the
+//    tree's loads and adds are unrolled for exactly the levels in use.
 // ===========================================================================
-template <int D>
+template <int D, int P>
 __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restrict__ partial,
                                                            const float* S_in, const float* z_in,
                                                            float* __restrict__ states, float* S_out,
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
   if (S_in != nullptr) running = (e < D * D) ? S_in[hb * D * D + e] : z_in[hb * D + (e - D * D)];
   const int sfirst = b * G.segs_item;   // this item's first segment
   const float* src = partial + ((size_t)h * G.nseg + sfirst) * G.cps1 * SZ + e;
-  if (G.cps1 == 1) {
+  if constexpr (P == 1) {
     // one partial per segment: the tree is the partial itself; the loads of
     // 8 segments are issued together
     constexpr int kBatch = 8;
@@ -78,15 +80,13 @@ __global__ __launch_bounds__(256) void state_reduce_kernel(const float* __restri
   } else {
     // levels of the 64-leaf tree at or above the chunk count add only zeros
     // (exactly), so they are skipped: the same sums in the same order
-    int P = 1;
-    while (P < G.cps1) P <<= 1;
+    static_assert(P <= kMaxChunks, "tree size");
     for (int s = 0; s < G.segs_item; ++s) {
-      float v[kMaxChunks];
+      float v[P];
 #pragma unroll
-      for (int i = 0; i < kMaxChunks; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
+      for (int i = 0; i < P; ++i) v[i] = (i < G.cps1) ? src[(size_t)(s * G.cps1 + i) * SZ] : 0.f;
 #pragma unroll
-      for (int w = kMaxChunks / 2; w >= 1; w >>= 1) {
-        if (w >= P) continue;
+      for (int w = P / 2; w >= 1; w >>= 1) {
 #pragma unroll
         for (int i = 0; i < w; ++i) v[i] += v[i + w];
       }
@@ -113,13 +113,26 @@ hipError_t launch_rope_table(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_state_reduce(const LaunchArgs& a) {
+template <int D, int P>
+static void launch_reduce_p(const LaunchArgs& a) {
   const Geometry& G = a.geo;
   constexpr int SZ = D * D + D;
   dim3 grid((SZ + 255) / 256, G.heads, G.batch);
-  hipLaunchKernelGGL((state_reduce_kernel<D>), grid, dim3(256), 0, a.stream, (const float*)a.partial, a.S_in, a.z_in,
-                     a.states, a.S_out, a.z_out, (bf16_t*)a.states_bf16, G);
+  hipLaunchKernelGGL((state_reduce_kernel<D, P>), grid, dim3(256), 0, a.stream, (const float*)a.partial, a.S_in,
+                     a.z_in, a.states, a.S_out, a.z_out, (bf16_t*)a.states_bf16, G);
+}
+
+template <int D>
+hipError_t launch_state_reduce(const LaunchArgs& a) {
+  const int c = a.geo.cps1;   // 1 .. kMaxChunks (the planner's bound)
+  if (c <= 1) launch_reduce_p<D, 1>(a);
+  else if (c <= 2) launch_reduce_p<D, 2>(a);
+  else if (c <= 4) launch_reduce_p<D, 4>(a);
+  else if (c <= 8) launch_reduce_p<D, 8>(a);
+  else if (c <= 16) launch_reduce_p<D, 16>(a);
+  else if (c <= 32) launch_reduce_p<D, 32>(a);
+  else if (c <= kMaxChunks) launch_reduce_p<D, kMaxChunks>(a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
