@@ -383,6 +383,10 @@ def main(argv=None):
     ap.add_argument("--batch", type=int, default=1,
                     help="independent sequences per call ([B, N, heads, d] tensors, items drawn with seeds "
                          "seed, seed + 1, ...); tokens/s and bytes count all items")
+    ap.add_argument("--plan", action="append", default=[], metavar="KNOB=VALUE",
+                    help="tuning only: set a launch-plan knob of the library (gla_internal.h; names as in "
+                         "gated_bidirectional_linear_amd.PLAN_KNOBS) for this run; the line records it in "
+                         "config.plan")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -433,13 +437,21 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    plan = {}
+    for kv in args.plan:
+        name, _, value = kv.partition("=")
+        if name not in gla.PLAN_KNOBS or not value.isdigit():
+            print(f"--plan {kv}: expected KNOB=VALUE with KNOB in {sorted(gla.PLAN_KNOBS)}", file=sys.stderr)
+            return 2
+        gla.plan_override(name, int(value))
+        plan[name] = int(value)
     w = WORKLOADS[args.workload]
     B = args.batch
     if B < 1:
         print("--batch must be at least 1", file=sys.stderr)
         return 2
     # profiles/ hold the default-dtype, single-sequence kernels
-    profiled = B == 1
+    profiled = B == 1 and not plan
     if args.dtype is not None:
         import dataclasses
         w = dataclasses.replace(w, dtype=args.dtype)
@@ -579,6 +591,7 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) q,k,v,g; beta=sigmoid(N(0,1)); rms_w=1+0.1N(0,1))",
         "config": {
             "workload": w.name,
+            **({"plan": plan} if plan else {}),
             "grid": f"{w.T}x{w.H}x{w.W}",
             "tokens": B * w.N,
             "heads": w.heads,

@@ -143,14 +143,13 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
   G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
 
-  // Heads per workgroup of pass 2 at d = 128.  bf16: four where the head count
-  // allows (1 KB token row segments), else pairs.  fp8: one head by default.  The
-  // four-head kernel also takes fp8 rows (512-byte segments), but fp8 halves the
-  // bytes per token while the vector work stays, and there its fixed split of
-  // waves into MFMA and stream roles leaves the MFMA waves idle: 548 us against
-  // 480 us for the one-head kernel at 720p/60s (the pair kernel's fp8
-  // instantiation spilled registers).  The knob reaches the four-head fp8 kernel.
-  const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, bf16_io ? 4 : 1);
+  // Heads per workgroup of pass 2 at d = 128: four where the head count allows
+  // (bf16: 1 KB token row segments; fp8: 512 bytes), else pairs for bf16 (the
+  // pair kernel's fp8 instantiation spilled registers) and one head for fp8.
+  // With fp8 rows the four-head kernel gives the feature work to its MFMA waves
+  // (the gate is a table lookup there): at 720p/60s 453 us against 453-464 us
+  // for the one-head kernel, and the whole call 825-836 us against 840-853 us.
+  const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, 4);
   G.pass2_pair = 0;
   if (narrow && d == 128 && !token_causal) {   // bf16 or fp8 I/O
     if (heads % 4 == 0 && max_hp >= 4) G.pass2_pair = 4;

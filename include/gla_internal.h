@@ -34,8 +34,8 @@ typedef enum {
   GLA_PLAN_TOKEN_CAUSAL_WORKGROUPS = 5,  /* > 0: (head, segment) units aimed for by the token-causal
                                             walk (segment length follows from it) */
   GLA_PLAN_PASS2_HEADS = 6,              /* > 0: at most this many heads per workgroup in the output
-                                            kernel (1, 2 or 4; defaults at d = 128: 4 for bf16, 1 for
-                                            fp8) and in the token-causal walk (1 or 2; default 2) */
+                                            kernel (1, 2 or 4; default 4 at d = 128) and in the
+                                            token-causal walk (1 or 2; default 2) */
   GLA_PLAN_NUM_KNOBS = 7
 } gla_plan_knob;
 

@@ -138,9 +138,9 @@ def test_fp8_binding_rejects_mixed_dtypes():
 
 @pytest.mark.parametrize("d", [128])
 def test_fp8_every_gate_code_four_heads(plan, d):
-    """Every finite e4m3 gate code through the four-head output kernel (chosen
-    by the plan knob: the one-head kernel is the fp8 default), whose MFMA waves
-    compute sigmoid(g) and pass it to the stream waves as fp16."""
+    """Every finite e4m3 gate code through the four-head output kernel (the
+    fp8 default for head counts divisible by 4), whose stream waves look
+    sigmoid(g) up in the LDS table of the 256 codes."""
     plan("pass2_heads", 4)
     T, H, W, heads = 4, 8, 9, 4
     inp = make_inputs(T, H, W, heads, d, "fp8", seed=42)
@@ -158,14 +158,17 @@ def test_fp8_every_gate_code_four_heads(plan, d):
 
 @pytest.mark.parametrize("shape", [(5, 9, 13, 4, 128), (1, 1, 1, 8, 128), (2, 5, 9, 12, 128)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_fp8_four_head_kernel_shapes(plan, shape):
-    """The four-head output kernel on fp8 rows (512-byte token segments)."""
-    plan("pass2_heads", 4)
+@pytest.mark.parametrize("heads_per_wg", [4, 1])
+def test_fp8_four_head_kernel_shapes(plan, shape, heads_per_wg):
+    """The four-head output kernel on fp8 rows (512-byte token segments; its
+    MFMA waves compute the features), and the one-head kernel on the same
+    shapes (chosen by the plan knob)."""
+    plan("pass2_heads", heads_per_wg)
     T, H, W, heads, d = shape
     inp = make_inputs(T, H, W, heads, d, "fp8", seed=44)
     got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
     err = fp8_excess(got, _oracle(inp))
-    _report(f"four-head kernel {shape}", err)
+    _report(f"{heads_per_wg}-head kernel {shape}", err)
     assert np.all(np.isfinite(got))
     assert err <= TOL["fp8"]
 
