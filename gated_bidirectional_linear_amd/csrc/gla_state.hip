@@ -313,7 +313,7 @@ struct Rows {
 struct Lane {
   int lane, m, h;
   uint32_t lane_off;        // byte offset of this lane's 4 channels in a step's row 8h
-  uint32_t beta_off;        // byte offset of beta of this lane's own token in a step
+  uint32_t beta_off;        // byte offset of beta of token (lane % 16) / 2 of this lane's half in a step
   uint32_t ROW;             // bytes between tokens
   uint32_t lane_rel;        // this lane's pair offset inside a table row (16-byte units)
   uint32_t ashift;          // bit offset of this lane's axis in the packed row offsets
@@ -329,7 +329,7 @@ __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
   L.h = L.lane >> 5;
   L.ROW = (uint32_t)G.heads * D * ES;
   L.lane_off = (uint32_t)(8 * L.h) * L.ROW + (uint32_t)ch.head * D * ES + 4u * ES * L.m;
-  L.beta_off = ((uint32_t)(8 * L.h + (L.lane & 7)) * (uint32_t)G.heads + (uint32_t)ch.head) * ES;
+  L.beta_off = ((uint32_t)(8 * L.h + ((L.lane & 15) >> 1)) * (uint32_t)G.heads + (uint32_t)ch.head) * ES;
   // pairs 2m and 2m+1 share an axis
   const int axis = (2 * L.m < R::PT) ? 0 : ((2 * L.m < R::PT + R::PY) ? 1 : 2);
   const int first = axis == 0 ? 0 : (axis == 1 ? R::PT : R::PT + R::PY);
@@ -421,26 +421,57 @@ __device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, co
     r.k[i] = Io<E>::bf16x4(raw.k[i]);
     r.v[i] = Io<E>::bf16x4(raw.v[i]);
   }
-  const int bsrc = Io<E>::beta_f32_bits(raw.b);
   // rotation words of the 8 tokens: all table reads issued together
   u32x4 cs[8];
-  float bt[8];
 #define GLA_FETCH(I)                                                                                 \
   {                                                                                                  \
     const uint32_t o = (uint32_t)row_bcast<I>((int)offs);                                            \
     cs[I] = *reinterpret_cast<const u32x4*>(rtab + 16 * (__builtin_amdgcn_ubfe(o, L.ashift, kOffBits) + L.lane_rel)); \
-    bt[I] = __int_as_float(row_bcast<I>(bsrc));                                                      \
   }
   GLA_FETCH(0) GLA_FETCH(1) GLA_FETCH(2) GLA_FETCH(3) GLA_FETCH(4) GLA_FETCH(5) GLA_FETCH(6) GLA_FETCH(7)
 #undef GLA_FETCH
-  // RMS factors: 4 channels per lane, 16 lanes per row, two rows per token
-  float inv[8];
+  // RMS factors.  Every lane holds 4 channels of each of its half's 8 tokens.
+  // A butterfly over the 16 lanes of a row halves the tokens a lane carries at
+  // every step (row_mirror pairs lane i with 15 - i, row_half_mirror i with
+  // 7 - i, quad_perm [3,2,1,0] i with i ^ 3, then [1,0,3,2] i with i ^ 1), so
+  // that lanes 2t and 2t + 1 of a row end with token t's sum over the row; the
+  // other row of the half is added, and each lane takes one reciprocal square
+  // root, of token t = (lane % 16) / 2, whose beta it also loaded.
+  float sq[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float ss = dot2bf(r.k[i].x, r.k[i].x, dot2bf(r.k[i].y, r.k[i].y, 0.f));
-    ss = pair_rows_sum(group_sum<16>(ss));
-    inv[i] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  for (int i = 0; i < 8; ++i) sq[i] = dot2bf(r.k[i].x, r.k[i].x, dot2bf(r.k[i].y, r.k[i].y, 0.f));
+  const int lr = L.lane & 15;
+  float s4[4], s2[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float keep = lr >= 8 ? sq[j + 4] : sq[j], send = lr >= 8 ? sq[j] : sq[j + 4];
+    s4[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x140, 0xF, 0xF, false));
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = (lr & 4) ? s4[j + 2] : s4[j], send = (lr & 4) ? s4[j] : s4[j + 2];
+    s2[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x141, 0xF, 0xF, false));
+  }
+  float s1;
+  {
+    const float keep = (lr & 2) ? s2[1] : s2[0], send = (lr & 2) ? s2[0] : s2[1];
+    s1 = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x1B, 0xF, 0xF, false));
+  }
+  s1 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xF, 0xF, false));
+  const float inv_own = __builtin_amdgcn_rsqf(pair_rows_sum(s1) * (1.0f / D) + eps);
+  const float sc_own = __int_as_float(Io<E>::beta_f32_bits(raw.b)) * inv_own;   // beta / rms
+  // the key sum's factors of token pair p as a bf16 pair, at lanes 4p, 4p + 1 of a row
+  const uint32_t ip_own =
+      pack2bf(inv_own, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(inv_own), 0x4E, 0xF, 0xF, false)));
+  // every token's scale, and every token pair's key-sum factors, from their lanes
+  float scs[8];
+  uint32_t ips[4];
+#define GLA_BCAST(I) scs[I] = __int_as_float(row_bcast<2 * I>(__float_as_int(sc_own)));
+  GLA_BCAST(0) GLA_BCAST(1) GLA_BCAST(2) GLA_BCAST(3) GLA_BCAST(4) GLA_BCAST(5) GLA_BCAST(6) GLA_BCAST(7)
+#undef GLA_BCAST
+#define GLA_BCAST(P) ips[P] = (uint32_t)row_bcast<4 * P>((int)ip_own);
+  GLA_BCAST(0) GLA_BCAST(1) GLA_BCAST(2) GLA_BCAST(3)
+#undef GLA_BCAST
   uint32_t kp[4][4];   // [channel slot c][token pair]
 #pragma unroll
   for (int ip = 0; ip < 4; ++ip) {
@@ -449,7 +480,7 @@ __device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, co
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = 2 * ip + j;
-      const float sc = bt[i] * inv[i];
+      const float sc = scs[i];
       const uint32_t p01 = relu2(r.k[i].x), p23 = relu2(r.k[i].y);
       rk2[j][0] = sc * dot2bf(p01, cs[i].x, 0.f);
       rk2[j][1] = sc * dot2bf(p01, cs[i].y, 0.f);
@@ -461,7 +492,7 @@ __device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, co
 #pragma unroll
     for (int c = 0; c < 4; ++c) kp[c][ip] = pack2bf(rk2[0][c], rk2[1][c]);
     // key sum: channel c of the token pair against (inv_a, inv_b)
-    const uint32_t ip2 = pack2bf(inv[2 * ip], inv[2 * ip + 1]);
+    const uint32_t ip2 = ips[ip];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t pa = ph2[0][c >> 1], pb = ph2[1][c >> 1];
