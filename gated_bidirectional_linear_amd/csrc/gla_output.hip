@@ -558,18 +558,83 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// E: bf16 rows (16 bytes per lane and 8 channels) or fp8 rows, e4m3 or e5m2 (8
-// bytes; a token's four heads are then 512 contiguous bytes per wave
-// instruction), widened to bf16 exactly for the features.
-//
-// The split of the per-token vector work between the two roles depends on the
-// gate type.  bf16 gates: the MFMA waves compute sigmoid(g) and hand it to the
-// stream waves through LDS as fp16; the stream waves compute the features of
-// the next tile and the epilogue of the previous one.  fp8 gates: sigmoid(g)
-// is a lookup in an LDS table of the 256 codes (in the region of the fp16 gate
-// tiles), so the MFMA waves take the features (and hand the denominators to
-// the stream waves through LDS) and the stream waves the gate reads and the
-// epilogue; either way both roles keep the vector unit busy.
+// The feature work of the four-head kernel for the waves that do it: R phi(q)
+// of this thread's 8 channels of token rw + TPI i (i < TPT) of each tile into
+// the rq buffer, and the denominators.  Row layout: wave w % 8 takes token w %
+// 8 of each round; lane -> head lane / 16, channels 8 (lane % 16) .. + 7.
+template <typename E>
+struct QuadFeatures {
+  using R = Rope<quad2::D>;
+  typedef typename BufRow<E>::Raw Raw;
+  float zc[8];               // key sums of this thread's channels
+  int axis, rbase, rstride, t_last, rw, hl, c16;
+  GridPos pos;               // of token rw of the next tile to prepare
+  int i_dt, i_dy, i_dx, t_dt, t_dy, t_dx;
+  const float2* tab;
+  __device__ __forceinline__ QuadFeatures(const float* zrow, int rw_, int hl_, int c16_, const typename R::View& rv,
+                                          long cbeg, long cend, const Geometry& G)
+      : rw(rw_), hl(hl_), c16(c16_), tab(rv.tab) {
+    using namespace quad2;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) zc[c] = zrow[8 * c16 + c];
+    t_last = cbeg < cend ? (int)((cend - 1) / (G.H * G.W)) : 0;
+    const int p0 = 4 * c16;   // this thread's 4 pairs share one axis
+    axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
+    rbase = axis == 0 ? p0 - rv.t_lo * R::PT
+          : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
+    rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+    const int HW = G.H * G.W;
+    pos.set((int)min(cbeg + rw, (long)G.N - 1), G.H, G.W);
+    i_dt = TPI / HW; i_dy = (TPI % HW) / G.W; i_dx = (TPI % HW) % G.W;
+    t_dt = TILE / HW; t_dy = (TILE % HW) / G.W; t_dx = (TILE % HW) % G.W;
+  }
+  // R phi(q) of the next tile (rows qt) into rq buffer rqb (bf16); its
+  // denominators phi(q) . z + eps r into den
+  __device__ __forceinline__ void run(const Raw (&qt)[quad2::TPT], bf16_t* rqb, const Geometry& G,
+                                      float (&den)[quad2::TPT]) {
+    using namespace quad2;
+    GridPos pp = pos;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tc = pp.t < t_last ? pp.t : t_last;
+      const int ps = axis == 0 ? tc : (axis == 1 ? pp.y : pp.x);
+      const f32x4* e = reinterpret_cast<const f32x4*>(tab + rbase + ps * rstride);
+      const f32x4 ca = e[0], cb = e[1];
+      typename R::CS cs;
+      cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
+      cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
+      pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
+      u32x4 u;   // 8 channels as bf16 pairs (fp8 widens exactly)
+      if constexpr (Elem<E>::is_f8) {
+        u = (u32x4){Elem<E>::template bf16_pair<false>(qt[i].x), Elem<E>::template bf16_pair<true>(qt[i].x),
+                    Elem<E>::template bf16_pair<false>(qt[i].y), Elem<E>::template bf16_pair<true>(qt[i].y)};
+      } else {
+        u = qt[i];
+      }
+      float ss = dot2sq(u.x, 0.f);
+      ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
+      const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
+      float ph[8];
+      Elem<bf16_t>::unpack(rl, ph);
+      float dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
+      ss = group_sum<16>(ss);
+      dp = group_sum<16>(dp);
+      const float ms = ss * (1.0f / D) + G.eps;
+      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
+      den[i] = dp + G.eps * r;
+      R::apply(ph, cs);
+      *reinterpret_cast<u32x4*>(rqb + (i * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) = Elem<bf16_t>::pack(ph);
+    }
+    pos.advance(t_dt, t_dy, t_dx, G.H, G.W);
+  }
+};
+
+// The four-head output kernel for bf16 rows (16 bytes per lane and 8
+// channels): the MFMA waves compute sigmoid(g) and hand it to the stream waves
+// through LDS as fp16; the stream waves compute the features of the next tile
+// and the epilogue of the previous one.
 template <typename E>
 __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void output_quad_kernel(
     const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
@@ -581,15 +646,11 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   constexpr uint32_t ES = sizeof(E);
   using R = Rope<D>;
   constexpr int SZ = D * D + D;
-  constexpr bool kF8 = Elem<E>::is_f8;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   bf16_t* rqs = reinterpret_cast<bf16_t*>(smem);                                    // [2][TILE][TOKQ]
   float* nums = reinterpret_cast<float*>(smem + 2 * RQ_BYTES);                      // [2][TILE][TOKN]
   uint16_t* sigs = reinterpret_cast<uint16_t*>(smem + 2 * RQ_BYTES + 2 * NUM_BYTES);  // [2][TILE][TOKQ] fp16
-  float* sig_tab = reinterpret_cast<float*>(sigs);                                   // fp8 gates: [256]
-  float* dens = sig_tab + 256;                       // fp8 gates: [4][TILE][HP], tile j in slot j & 3
   float2* ropel = reinterpret_cast<float2*>(smem + 4 * RQ_BYTES + 2 * NUM_BYTES);
-  static_assert(kF8 ? (256 + 4 * TILE * HP) * 4 <= 2 * RQ_BYTES : true, "fp8 gate table and denominators");
 
   // chunk-major over head quads: consecutive ids take the same token range
   const int nquads = G.heads / HP;
@@ -628,84 +689,6 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + rw) * ROW + (uint32_t)hl * D * ES + 8u * ES * c16;
 
   const typename R::View rv = rope_view<D, true>(ropel, rope, G, cbeg, cend);
-  if constexpr (kF8) fill_sigmoid_fp8<E>(sig_tab, tid, THREADS);   // read after the first barrier
-
-  // ---- features: R phi(q) of a tile into rq and its denominators (the role
-  //      named above) ----
-  const bool feature_role = kF8 ? wave < NMW : wave >= NMW;
-  const float* zrow = states + ((size_t)seg * G.heads + h0 + hl) * SZ + D * D;
-  float zc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) zc[c] = zrow[8 * c16 + c];
-  const int t_last = cbeg < cend ? (int)((cend - 1) / (G.H * G.W)) : 0;
-  const int p0 = 4 * c16;   // this thread's 4 pairs share one axis
-  const int axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
-  const int rbase = axis == 0 ? p0 - rv.t_lo * R::PT
-                  : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
-  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
-  const int HW = G.H * G.W;
-  GridPos pos;   // of token rw of the next tile to prepare; a thread's tokens are TPI apart
-  pos.set((int)min(cbeg + rw, (long)G.N - 1), G.H, G.W);
-  const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
-  const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
-
-  Raw qr[QDEPTH][TPT];
-  auto issue_q = [&](Raw (&r)[TPT], long t0) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
-  };
-  if (feature_role) {
-#pragma unroll
-    for (int d = 0; d < QDEPTH; ++d) issue_q(qr[d], cbeg + d * TILE);
-  }
-
-  float den[2][TPT];   // denominators of the tiles in flight, by parity (bf16 gates)
-  // R phi(q) of tile j into rq buffer j & 1 (bf16) and its denominators
-  auto features = [&](Raw (&qt)[TPT], int j) {
-    const int b = j & 1;
-    GridPos pp = pos;
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int tc = pp.t < t_last ? pp.t : t_last;
-      const int ps = axis == 0 ? tc : (axis == 1 ? pp.y : pp.x);
-      const f32x4* e = reinterpret_cast<const f32x4*>(rv.tab + rbase + ps * rstride);
-      const f32x4 ca = e[0], cb = e[1];
-      typename R::CS cs;
-      cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
-      cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
-      pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
-      u32x4 u;   // 8 channels as bf16 pairs (fp8 widens exactly)
-      if constexpr (kF8) {
-        u = (u32x4){Elem<E>::template bf16_pair<false>(qt[i].x), Elem<E>::template bf16_pair<true>(qt[i].x),
-                    Elem<E>::template bf16_pair<false>(qt[i].y), Elem<E>::template bf16_pair<true>(qt[i].y)};
-      } else {
-        u = qt[i];
-      }
-      float ss = dot2sq(u.x, 0.f);
-      ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
-      const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
-      float ph[8];
-      Elem<bf16_t>::unpack(rl, ph);
-      float dp = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
-      ss = group_sum<16>(ss);
-      dp = group_sum<16>(dp);
-      const float ms = ss * (1.0f / D) + G.eps;
-      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
-      const float dn = dp + G.eps * r;
-      if constexpr (kF8) {
-        if (c16 == 0) dens[((j & 3) * TILE + i * TPI + rw) * HP + hl] = dn;
-      } else {
-        den[b][i] = dn;
-      }
-      R::apply(ph, cs);
-      *reinterpret_cast<u32x4*>(rqs + (size_t)b * (TILE * TOKQ) + (i * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) =
-          Elem<bf16_t>::pack(ph);
-    }
-    pos.advance(t_dt, t_dy, t_dx, G.H, G.W);
-  };
 
   if (wave < NMW) {
     // ------------------------------ MFMA waves ------------------------------
@@ -718,10 +701,8 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
     };
-    if constexpr (!kF8) {
 #pragma unroll
-      for (int d = 0; d < GDEPTH; ++d) issue_g(gr[d], cbeg + d * TILE);
-    }
+    for (int d = 0; d < GDEPTH; ++d) issue_g(gr[d], cbeg + d * TILE);
     // A[i = v row vh + 16 mt + r16][k = 32 ks + 8 k8 + j] of the 16x16x32 MFMA
     const bf16_t* Sb = states_bf16 + ((size_t)seg * G.heads + h0 + m) * (D * D);
     bf16x8_t sf[4][4];
@@ -731,11 +712,7 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       for (int ks = 0; ks < 4; ++ks)
         sf[mt][ks] = __builtin_bit_cast(bf16x8_t,
                                         *reinterpret_cast<const u32x4*>(Sb + (size_t)(vh + 16 * mt + r16) * D + 32 * ks + 8 * k8));
-    lds_barrier();   // RoPE rows (and the gate table) staged
-    if constexpr (kF8) {
-      features(qr[0], 0);
-      issue_q(qr[0], cbeg + QDEPTH * TILE);
-    }
+    lds_barrier();   // RoPE rows staged
     lds_barrier();   // rq of tile 0 written
     for (int i0 = 0; i0 < ntiles; i0 += GDEPTH) {
 #pragma unroll
@@ -758,29 +735,278 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
           for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mt][ks], bfr[ks], acc, 0, 0, 0);
           *reinterpret_cast<f32x4*>(nb + r16 * TOKN + m * NUM_PITCH + vh + 16 * mt + 4 * k8) = acc;
         }
-        if constexpr (kF8) {
-          // features of tile i + 1 (past the chunk its rows read as zero)
-          features(qr[(d + 1) % QDEPTH], i + 1);
-          issue_q(qr[(d + 1) % QDEPTH], t0 + TILE + QDEPTH * TILE);
-        } else {
-          // sigmoid(g) of tile i, row layout, fp16
-          uint16_t* sb = sigs + (size_t)(i & 1) * (TILE * TOKQ);
+        // sigmoid(g) of tile i, row layout, fp16
+        uint16_t* sb = sigs + (size_t)(i & 1) * (TILE * TOKQ);
 #pragma unroll
-          for (int j = 0; j < TPT; ++j) {
-            float gv[8];
-            Elem<E>::unpack(gr[d][j], gv);
-            uint32_t w[4];
+        for (int j = 0; j < TPT; ++j) {
+          float gv[8];
+          Elem<E>::unpack(gr[d][j], gv);
+          uint32_t w[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float sg0 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c]));
-              const float sg1 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c + 1]));
-              w[c] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){sg0, sg1}, f16x2_t));
-            }
-            *reinterpret_cast<u32x4*>(sb + (j * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) =
-                (u32x4){w[0], w[1], w[2], w[3]};
+          for (int c = 0; c < 4; ++c) {
+            const float s0 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c]));
+            const float s1 = __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * c + 1]));
+            w[c] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){s0, s1}, f16x2_t));
           }
-          issue_g(gr[d], t0 + GDEPTH * TILE);
+          *reinterpret_cast<u32x4*>(sb + (j * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) = (u32x4){w[0], w[1], w[2], w[3]};
         }
+        issue_g(gr[d], t0 + GDEPTH * TILE);
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ------------------------------ stream waves ------------------------------
+  const float* zrow = states + ((size_t)seg * G.heads + h0 + hl) * SZ + D * D;
+  float zc[8], wc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    zc[c] = zrow[8 * c16 + c];
+    wc[c] = rms_w[8 * c16 + c];
+  }
+  const int t_last = cbeg < cend ? (int)((cend - 1) / (G.H * G.W)) : 0;
+  const int p0 = 4 * c16;   // this thread's 4 pairs share one axis
+  const int axis = (p0 < R::PT) ? 0 : ((p0 < R::PT + R::PY) ? 1 : 2);
+  const int rbase = axis == 0 ? p0 - rv.t_lo * R::PT
+                  : (axis == 1 ? rv.nt * R::PT + (p0 - R::PT) : rv.nt * R::PT + rv.H * R::PY + (p0 - R::PT - R::PY));
+  const int rstride = axis == 0 ? R::PT : (axis == 1 ? R::PY : R::PX);
+  const int HW = G.H * G.W;
+  GridPos pos;   // of token rw of the next tile to prepare; a thread's tokens are TPI apart
+  pos.set((int)min(cbeg + rw, (long)G.N - 1), G.H, G.W);
+  const int i_dt = TPI / HW, i_dy = (TPI % HW) / G.W, i_dx = (TPI % HW) % G.W;
+  const int t_dt = TILE / HW, t_dy = (TILE % HW) / G.W, t_dx = (TILE % HW) % G.W;
+
+  Raw qr[QDEPTH][TPT];
+  auto issue_q = [&](Raw (&r)[TPT], long t0) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(q, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
+  };
+#pragma unroll
+  for (int d = 0; d < QDEPTH; ++d) issue_q(qr[d], cbeg + d * TILE);
+
+  float den[2][TPT];   // denominators of the tiles in flight, by parity
+  // R phi(q) of a tile into rq buffer b (bf16) and its denominators
+  auto features = [&](Raw (&qt)[TPT], int b) {
+    GridPos pp = pos;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tc = pp.t < t_last ? pp.t : t_last;
+      const int ps = axis == 0 ? tc : (axis == 1 ? pp.y : pp.x);
+      const f32x4* e = reinterpret_cast<const f32x4*>(rv.tab + rbase + ps * rstride);
+      const f32x4 ca = e[0], cb = e[1];
+      typename R::CS cs;
+      cs.c[0] = ca.x; cs.s[0] = ca.y; cs.c[1] = ca.z; cs.s[1] = ca.w;
+      cs.c[2] = cb.x; cs.s[2] = cb.y; cs.c[3] = cb.z; cs.s[3] = cb.w;
+      pp.advance(i_dt, i_dy, i_dx, G.H, G.W);
+      u32x4 u;   // 8 channels as bf16 pairs (fp8 widens exactly)
+      if constexpr (Elem<E>::is_f8) {
+        u = (u32x4){Elem<E>::template bf16_pair<false>(qt[i].x), Elem<E>::template bf16_pair<true>(qt[i].x),
+                    Elem<E>::template bf16_pair<false>(qt[i].y), Elem<E>::template bf16_pair<true>(qt[i].y)};
+      } else {
+        u = qt[i];
+      }
+      float ss = dot2sq(u.x, 0.f);
+      ss = dot2sq(u.y, ss); ss = dot2sq(u.z, ss); ss = dot2sq(u.w, ss);
+      const u32x4 rl = {relu2(u.x), relu2(u.y), relu2(u.z), relu2(u.w)};
+      float ph[8];
+      Elem<bf16_t>::unpack(rl, ph);
+      float dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dp += ph[c] * zc[c];
+      ss = group_sum<16>(ss);
+      dp = group_sum<16>(dp);
+      const float ms = ss * (1.0f / D) + G.eps;
+      const float r = ms * __builtin_amdgcn_rsqf(ms);   // sqrt(ms) without the IEEE sqrt sequence
+      den[b][i] = dp + G.eps * r;
+      R::apply(ph, cs);
+      *reinterpret_cast<u32x4*>(rqs + (size_t)b * (TILE * TOKQ) + (i * TPI + rw) * TOKQ + hl * RQ_PITCH + 8 * c16) =
+          Elem<bf16_t>::pack(ph);
+    }
+    pos.advance(t_dt, t_dy, t_dx, G.H, G.W);
+  };
+  // gate, RMSNorm and store of the tile at t0 from buffers b
+  auto epilogue = [&](int b, long t0) {
+    const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, t0);
+    const float* nb = nums + (size_t)b * (TILE * TOKN);
+    const uint16_t* sb = sigs + (size_t)b * (TILE * TOKQ);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int tok = i * TPI + rw;
+      const float* src = nb + tok * TOKN + hl * NUM_PITCH + 8 * c16;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(src + 4);
+      const u32x4 sw = *reinterpret_cast<const u32x4*>(sb + tok * TOKQ + hl * RQ_PITCH + 8 * c16);
+      const float nm[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
+      const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+      float y[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {   // sigmoid(g) * num, one v_fma_mix_f32 each
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, sv[c]);
+        y[2 * c] = fmaf((float)h.x, nm[2 * c], 0.0f);
+        y[2 * c + 1] = fmaf((float)h.y, nm[2 * c + 1], 0.0f);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ss += y[c] * y[c];
+      ss = group_sum<16>(ss);
+      const float scale = out_scale(ss * (1.0f / D), den[b][i], G.eps);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = wc[c] * y[c] * scale;
+      BR::store(ors, voff[i], 0, Elem<E>::pack(y));   // rows past the chunk are dropped
+    }
+  };
+
+  lds_barrier();   // RoPE rows staged
+  features(qr[0], 0);
+  issue_q(qr[0], cbeg + QDEPTH * TILE);
+  lds_barrier();   // rq of tile 0 written
+  // step i: the MFMA waves take tile i; the stream waves finish tile i - 1 and
+  // prepare tile i + 1 (past the chunk its rows read as zero)
+  for (int i0 = 0; i0 < ntiles; i0 += QDEPTH) {
+#pragma unroll
+    for (int d = 0; d < QDEPTH; ++d) {
+      const int i = i0 + d;
+      if (i >= ntiles) break;   // uniform over the workgroup
+      const long t0 = cbeg + (long)i * TILE;
+      if (i >= 1) epilogue((i - 1) & 1, t0 - TILE);
+      features(qr[(d + 1) % QDEPTH], (i + 1) & 1);
+      issue_q(qr[(d + 1) % QDEPTH], t0 + TILE + QDEPTH * TILE);
+      lds_barrier();
+    }
+  }
+  if (ntiles > 0) epilogue((ntiles - 1) & 1, cbeg + (long)(ntiles - 1) * TILE);
+}
+
+// The four-head output kernel for fp8 rows (e4m3 or e5m2: 8 bytes per lane and
+// 8 channels, a token's four heads 512 contiguous bytes per wave instruction),
+// widened to bf16 exactly for the features.  With one-byte gates sigmoid(g)
+// is a lookup in an LDS table of the 256 codes, so the roles split the vector
+// work the other way round from the bf16 kernel above: the MFMA waves compute
+// the next tile's features (R phi(q) and the denominators, handed to the
+// stream waves through LDS) besides the numerators, and the stream waves read
+// the gates and run the epilogue.
+template <typename E>
+__global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void output_quad_f8_kernel(
+    const E* __restrict__ q, const E* __restrict__ g, const float* __restrict__ states,
+    const bf16_t* __restrict__ states_bf16, const float* __restrict__ rms_w, const float2* __restrict__ rope,
+    E* __restrict__ out, Geometry G) {
+  using namespace quad2;
+  static_assert(Elem<E>::is_f8, "one-byte rows");
+  using BR = BufRow<E>;
+  typedef typename BR::Raw Raw;
+  constexpr uint32_t ES = sizeof(E);
+  using R = Rope<D>;
+  constexpr int SZ = D * D + D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  bf16_t* rqs = reinterpret_cast<bf16_t*>(smem);                                    // [2][TILE][TOKQ]
+  float* nums = reinterpret_cast<float*>(smem + 2 * RQ_BYTES);                      // [2][TILE][TOKN]
+  float* sig_tab = reinterpret_cast<float*>(smem + 2 * RQ_BYTES + 2 * NUM_BYTES);   // [256]
+  float* dens = sig_tab + 256;                             // [4][TILE][HP], tile j in slot j & 3
+  float2* ropel = reinterpret_cast<float2*>(smem + 4 * RQ_BYTES + 2 * NUM_BYTES);
+  static_assert((256 + 4 * TILE * HP) * 4 <= 2 * RQ_BYTES, "gate table and denominators");
+
+  // chunk-major over head quads: consecutive ids take the same token range
+  const int nquads = G.heads / HP;
+  const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int ci = lin / nquads;
+  const int quad = lin - ci * nquads;
+  const int seg = ci / G.cps2;
+  long s0, s1;
+  seg_bounds(G, seg, s0, s1);
+  const long cbeg = min(s0 + (long)(ci - seg * G.cps2) * G.chunk2, s1);
+  const long cend = min(cbeg + (long)G.chunk2, s1);
+  const int h0 = HP * quad;
+  const int ntiles = (int)((cend - cbeg + TILE - 1) / TILE);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  // row layout (both roles): wave w % 8 takes token w % 8 of each round; lane -> head lane / 16,
+  // channels 8 (lane % 16) .. + 7
+  const int rw = wave & 7;
+  const int hl = lane >> 4;
+  const int c16 = lane & 15;
+  // Tile loads and stores go through buffer resources based at the tile's first
+  // row and this quad, ending at the chunk's last row: rows past it read as zero
+  // and stores to them are dropped.
+  const uint32_t ROW = (uint32_t)G.heads * D * ES;
+  const uint32_t quad_off = (uint32_t)h0 * D * ES;
+  auto tile_rsrc = [&](const void* p, long t0) {
+    const long left = cend - t0;
+    const uint32_t rows = left <= 0 ? 0u : (left >= TILE ? (uint32_t)TILE : (uint32_t)left);
+    const uint32_t bytes = rows == 0 ? 0u : rows * ROW - quad_off;   // the last row ends at this quad's channels
+    return make_rsrc(reinterpret_cast<const char*>(p) + (size_t)t0 * ROW + quad_off, bytes);
+  };
+  uint32_t voff[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) voff[i] = (uint32_t)(i * TPI + rw) * ROW + (uint32_t)hl * D * ES + 8u * ES * c16;
+  // rows of tile t0 of tensor p
+  auto issue = [&](const E* p, Raw (&r)[TPT], long t0) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(p, t0);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
+  };
+
+  const typename R::View rv = rope_view<D, true>(ropel, rope, G, cbeg, cend);
+  fill_sigmoid_fp8<E>(sig_tab, tid, THREADS);   // read after the first barrier
+
+  if (wave < NMW) {
+    // ------------------------------ MFMA waves ------------------------------
+    const int m = wave >> 1;            // head within the quad
+    const int vh = 64 * (wave & 1);     // first v row of this wave
+    const int r16 = lane & 15, k8 = lane >> 4;
+    Raw qr[QDEPTH][TPT];
+#pragma unroll
+    for (int d = 0; d < QDEPTH; ++d) issue(q, qr[d], cbeg + d * TILE);
+    QuadFeatures<E> feat(states + ((size_t)seg * G.heads + h0 + hl) * SZ + D * D, rw, hl, c16, rv, cbeg, cend, G);
+    // R phi(q) of tile j into rq buffer j & 1, its denominators into LDS slot j & 3
+    auto features = [&](Raw (&qt)[TPT], int j) {
+      float dn[TPT];
+      feat.run(qt, rqs + (size_t)(j & 1) * (TILE * TOKQ), G, dn);
+      if (c16 == 0) {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) dens[((j & 3) * TILE + i * TPI + rw) * HP + hl] = dn[i];
+      }
+    };
+    // A[i = v row vh + 16 mt + r16][k = 32 ks + 8 k8 + j] of the 16x16x32 MFMA
+    const bf16_t* Sb = states_bf16 + ((size_t)seg * G.heads + h0 + m) * (D * D);
+    bf16x8_t sf[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sf[mt][ks] = __builtin_bit_cast(bf16x8_t,
+                                        *reinterpret_cast<const u32x4*>(Sb + (size_t)(vh + 16 * mt + r16) * D + 32 * ks + 8 * k8));
+    lds_barrier();   // RoPE rows and the gate table staged
+    features(qr[0], 0);
+    issue(q, qr[0], cbeg + QDEPTH * TILE);
+    lds_barrier();   // rq of tile 0 written
+    for (int i0 = 0; i0 < ntiles; i0 += QDEPTH) {
+#pragma unroll
+      for (int d = 0; d < QDEPTH; ++d) {
+        const int i = i0 + d;
+        if (i >= ntiles) break;   // uniform over the workgroup
+        const long t0 = cbeg + (long)i * TILE;
+        // numerators of tile i: num^T = S RQ^T, D[v = vh + 16 mt + 4 k8 + r][token r16]
+        const bf16_t* rqb = rqs + (size_t)(i & 1) * (TILE * TOKQ);
+        float* nb = nums + (size_t)(i & 1) * (TILE * TOKN);
+        bf16x8_t bfr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          bfr[ks] = __builtin_bit_cast(bf16x8_t,
+                                       *reinterpret_cast<const u32x4*>(rqb + r16 * TOKQ + m * RQ_PITCH + 32 * ks + 8 * k8));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf[mt][ks], bfr[ks], acc, 0, 0, 0);
+          *reinterpret_cast<f32x4*>(nb + r16 * TOKN + m * NUM_PITCH + vh + 16 * mt + 4 * k8) = acc;
+        }
+        // features of tile i + 1 (past the chunk its rows read as zero)
+        features(qr[(d + 1) % QDEPTH], i + 1);
+        issue(q, qr[(d + 1) % QDEPTH], t0 + TILE + QDEPTH * TILE);
         lds_barrier();
       }
     }
@@ -791,25 +1017,16 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
   float wc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) wc[c] = rms_w[8 * c16 + c];
-  // fp8 gates of the tiles whose epilogue is next: tile j in slot j & 1, read
-  // two steps after it is requested (the step loop below is unrolled by two)
+  // gates of the tiles whose epilogue is next: tile j in slot j & 1, read two
+  // steps after it is requested (the step loop below is unrolled by two)
   static_assert(QDEPTH == 2, "gate slots follow the two-tile unroll");
   Raw gq[2][TPT];
-  auto issue_gq = [&](Raw (&r)[TPT], long t0) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(g, t0);
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) r[i] = BR::load(rs, voff[i], 0);
-  };
-  if constexpr (kF8) {
-    issue_gq(gq[0], cbeg);
-    issue_gq(gq[1], cbeg + TILE);
-  }
-  // gate, RMSNorm and store of tile j (fp8: gates gt)
+  issue(g, gq[0], cbeg);
+  issue(g, gq[1], cbeg + TILE);
+  // gate, RMSNorm and store of tile j (gates gt)
   auto epilogue = [&](int j, const Raw (&gt)[TPT]) {
-    const int b = j & 1;
     const __amdgpu_buffer_rsrc_t ors = tile_rsrc(out, cbeg + (long)j * TILE);
-    const float* nb = nums + (size_t)b * (TILE * TOKN);
-    const uint16_t* sb = sigs + (size_t)b * (TILE * TOKQ);
+    const float* nb = nums + (size_t)(j & 1) * (TILE * TOKN);
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int tok = i * TPI + rw;
@@ -818,22 +1035,9 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       const f32x4 bb = *reinterpret_cast<const f32x4*>(src + 4);
       const float nm[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
       float y[8];
-      float dn;
-      if constexpr (kF8) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) y[c] = nm[c] * sigmoid_fp8(sig_tab, c < 4 ? gt[i].x : gt[i].y, c & 3);
-        dn = dens[((j & 3) * TILE + tok) * HP + hl];
-      } else {
-        const u32x4 sw = *reinterpret_cast<const u32x4*>(sb + tok * TOKQ + hl * RQ_PITCH + 8 * c16);
-        const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {   // sigmoid(g) * num, one v_fma_mix_f32 each
-          const f16x2_t h = __builtin_bit_cast(f16x2_t, sv[c]);
-          y[2 * c] = fmaf((float)h.x, nm[2 * c], 0.0f);
-          y[2 * c + 1] = fmaf((float)h.y, nm[2 * c + 1], 0.0f);
-        }
-        dn = den[b][i];
-      }
+      for (int c = 0; c < 8; ++c) y[c] = nm[c] * sigmoid_fp8(sig_tab, c < 4 ? gt[i].x : gt[i].y, c & 3);
+      const float dn = dens[((j & 3) * TILE + tok) * HP + hl];
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) ss += y[c] * y[c];
@@ -845,14 +1049,9 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  lds_barrier();   // RoPE rows (and the gate table) staged
-  if constexpr (!kF8) {
-    features(qr[0], 0);
-    issue_q(qr[0], cbeg + QDEPTH * TILE);
-  }
+  lds_barrier();   // RoPE rows and the gate table staged
   lds_barrier();   // rq of tile 0 written
-  // step i: the MFMA waves take tile i; the stream waves finish tile i - 1
-  // and (bf16 gates) prepare tile i + 1 (past the chunk its rows read as zero)
+  // step i: the MFMA waves take tile i and prepare tile i + 1; the stream waves finish tile i - 1
   for (int i0 = 0; i0 < ntiles; i0 += QDEPTH) {
 #pragma unroll
     for (int d = 0; d < QDEPTH; ++d) {
@@ -862,11 +1061,7 @@ __global__ __launch_bounds__(quad2::THREADS) __attribute__((amdgpu_waves_per_eu(
       if (i >= 1) {
         // tile i - 1 (gate slot (d + 1) & 1, as i0 is even); the slot then takes tile i + 1
         epilogue(i - 1, gq[(d + 1) & 1]);
-        if constexpr (kF8) issue_gq(gq[(d + 1) & 1], t0 + TILE);
-      }
-      if constexpr (!kF8) {
-        features(qr[(d + 1) % QDEPTH], i + 1);
-        issue_q(qr[(d + 1) % QDEPTH], t0 + TILE + QDEPTH * TILE);
+        issue(g, gq[(d + 1) & 1], t0 + TILE);
       }
       lds_barrier();
     }
@@ -884,9 +1079,15 @@ hipError_t launch_output(const LaunchArgs& a) {
     // the planner sets pass2_pair to 4 (bf16 or fp8) only for a head count divisible by 4
     // (and gives states_bf16), to 2 (bf16) only for an even one, both with the RoPE rows in LDS
     if (G.pass2_pair == 4) {
-      hipLaunchKernelGGL((output_quad_kernel<E>), dim3((G.heads / 4) * G.nseg * G.cps2), dim3(quad2::THREADS), 0,
-                         a.stream, (const E*)a.q, (const E*)a.g, (const float*)a.states, a.states_bf16, a.rms_w,
-                         (const float2*)a.rope, (E*)a.out, G);
+      const dim3 grid((G.heads / 4) * G.nseg * G.cps2);
+      if constexpr (Elem<E>::is_f8)
+        hipLaunchKernelGGL((output_quad_f8_kernel<E>), grid, dim3(quad2::THREADS), 0, a.stream, (const E*)a.q,
+                           (const E*)a.g, (const float*)a.states, a.states_bf16, a.rms_w, (const float2*)a.rope,
+                           (E*)a.out, G);
+      else
+        hipLaunchKernelGGL((output_quad_kernel<E>), grid, dim3(quad2::THREADS), 0, a.stream, (const E*)a.q,
+                           (const E*)a.g, (const float*)a.states, a.states_bf16, a.rms_w, (const float2*)a.rope,
+                           (E*)a.out, G);
       return hipGetLastError();
     }
   }
