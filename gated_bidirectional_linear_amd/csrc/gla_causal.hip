@@ -58,7 +58,8 @@ struct CausalCfg {
   static constexpr int AM_OFF = VT_OFF + (TR ? TT * RPV : D * CP) * (int)sizeof(L);
   // Key sums.  Head pairs (bf16 operands) take the denominator's intra-tile
   // part and the tile's key sums on MFMA from bf16 rows of phi(q) ([TT][RP])
-  // and phi(k^) ([TT][RPK]), keeping the intra-tile denominators [TT] and the
+  // and phi(k) = relu(k) ([TT][RPK]; each token's RMS factor [TT] is applied
+  // in those products), keeping the intra-tile denominators [TT] and the
   // tile's key sums [D] in fp32; otherwise phi(k^) is scanned in fp32
   // ([TT][FP]), which keeps a single head's LDS small enough for two
   // workgroups per CU.
@@ -67,7 +68,8 @@ struct CausalCfg {
   static constexpr int PHK_OFF = ZK_OFF + TT * RP * 2;
   static constexpr int DIN_OFF = PHK_OFF + TT * RPK * 2;
   static constexpr int ZS_OFF = DIN_OFF + TT * 4;
-  static constexpr int ZK_BYTES = MD ? (TT * RP + TT * RPK) * 2 + (TT + D) * 4 : TT * FP * 4;
+  static constexpr int INV_OFF = ZS_OFF + D * 4;
+  static constexpr int ZK_BYTES = MD ? (TT * RP + TT * RPK) * 2 + (TT + D + TT) * 4 : TT * FP * 4;
   static constexpr int NUM_OFF = ZK_OFF + ZK_BYTES;
   static constexpr int SMEM = NUM_OFF + TT * FP * 4;        // per head
   static constexpr int ROPE = kRopeLdsEntriesCausal * 8;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   //   vT   [TT][RPV]  v rows (bf16 operands) or [D][CP] v transposed
   //   am   [TT][CP]   masked rk_j . rq_i, row i
   //   zk   [TT][FP]   phi k^, then its running sums (fp32 scan), or
-  //   phqs [TT][RP], phks [TT][RPK], dins [TT], zsum [D] (MFMA key sums; see CausalCfg)
+  //   phqs [TT][RP], phks [TT][RPK], dins [TT], zsum [D], invs [TT] (MFMA key sums; see CausalCfg)
   //   nums [TT][FP]   numerators (token, v channel), fp32
   auto rqs = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RQ_OFF); };
   auto rks = [&](int h) { return reinterpret_cast<L*>(smem + h * C::SMEM + C::RK_OFF); };
@@ -237,6 +239,7 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
   auto phks = [&](int h) { return reinterpret_cast<bf16_t*>(smem + h * C::SMEM + C::PHK_OFF); };
   auto dins = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::DIN_OFF); };
   auto zsum = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::ZS_OFF); };
+  auto invs = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::INV_OFF); };
   auto nums = [&](int h) { return reinterpret_cast<float*>(smem + h * C::SMEM + C::NUM_OFF); };
 
   // workgroup -> (head group, segment), head groups of a segment consecutive
@@ -424,8 +427,10 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
             rk[2 * j + 1] = bi * dot2bf(kl[j], wb[j], 0.f);
             phq[i][2 * j] = bf16lo(ql[j]);
             phq[i][2 * j + 1] = bf16hi(ql[j]);
-            pk[2 * j] = bf16lo(kl[j]) * inv;                // phi(k^)
-            pk[2 * j + 1] = bf16hi(kl[j]) * inv;
+            if constexpr (!C::MD) {
+              pk[2 * j] = bf16lo(kl[j]) * inv;                // phi(k^)
+              pk[2 * j + 1] = bf16hi(kl[j]) * inv;
+            }
           }
           if constexpr (C::MD) {
             // the denominator's part from the key sums before this tile
@@ -434,7 +439,9 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
             for (int c = 0; c < 8; ++c) dz += phq[i][c] * zr[c];
             dpz[i] = group_sum<C::CG>(dz);
             *reinterpret_cast<u32x4*>(phqs(hl) + tok * C::RP + 8 * cg) = (u32x4){ql[0], ql[1], ql[2], ql[3]};
-            *reinterpret_cast<u32x4*>(phks(hl) + tok * C::RPK + 8 * cg) = Elem<bf16_t>::pack(pk);
+            // relu(k) as read; the RMS factor is applied in the key-sum products
+            *reinterpret_cast<u32x4*>(phks(hl) + tok * C::RPK + 8 * cg) = (u32x4){kl[0], kl[1], kl[2], kl[3]};
+            if (cg == 0) invs(hl)[tok] = inv;
           } else {
             float* zrow = zk(hl) + tok * C::FP + 8 * cg;
             *reinterpret_cast<f32x4*>(zrow) = (f32x4){pk[0], pk[1], pk[2], pk[3]};
@@ -527,7 +534,8 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
     }
     if constexpr (C::MD) {
       if (ww == 1) {
-        // intra-tile denominators: P^T[j][i] = phi(k^_j) . phi(q_i) on MFMA,
+        // intra-tile denominators: P^T[j][i] = phi(k_j) . phi(q_i) on MFMA,
+        // each row j times token j's RMS factor (phi(k^_j) = inv_j phi(k_j)),
         // masked like the scores and summed over j (16 registers, then the
         // other lane half through v_permlane32_swap)
         f32x16 a = {};
@@ -539,24 +547,35 @@ __global__ __launch_bounds__((CausalCfg<D, E, HP>::THREADS), (CausalCfg<D, E, HP
         }
         float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool keep = incl ? j <= l32 : j < l32;
-          part += keep ? a[r] : 0.f;
+        for (int rb = 0; rb < 4; ++rb) {
+          const f32x4 iv = *reinterpret_cast<const f32x4*>(invs(hw) + 8 * rb + 4 * hi);   // rows 8 rb + 4 hi + 0..3
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 8 * rb + 4 * hi + r;
+            const bool keep = incl ? j <= l32 : j < l32;
+            part += keep ? a[4 * rb + r] * iv[r] : 0.f;
+          }
         }
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         if (hi == 0) dins(hw)[l32] = part + __uint_as_float(sw[1]);
       } else if (ww == 2) {
-        // the tile's key sums per channel: ones x phi(K^) on MFMA (every row of
-        // the product holds the column sums)
-        const uint4 ones4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
-        const typename M::frag ones = __builtin_bit_cast(bf16x8, ones4);
+        // the tile's key sums per channel: (RMS factors) x phi(K) on MFMA,
+        // sum over j of inv_j phi(k_j) = phi(k^_j) (every row of the product
+        // holds the column sums)
+        typename M::frag fi[TT / M::KSTEP];   // A[m][k = token 16 ks + 8 hi + e] = inv of that token, bf16
+#pragma unroll
+        for (int ks = 0; ks < TT / M::KSTEP; ++ks) {
+          const f32x4 ia = *reinterpret_cast<const f32x4*>(invs(hw) + ks * M::KSTEP + M::KPL * hi);
+          const f32x4 ib = *reinterpret_cast<const f32x4*>(invs(hw) + ks * M::KSTEP + M::KPL * hi + 4);
+          const float iv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+          fi[ks] = M::from_f32(iv);
+        }
 #pragma unroll
         for (int ct = 0; ct < C::MT; ++ct) {
           f32x16 a = {};
 #pragma unroll
           for (int ks = 0; ks < TT / M::KSTEP; ++ks)
-            a = M::mma(ones, tr_frag(phks(hw), C::RPK, ks * M::KSTEP, 32 * ct, lane), a);
+            a = M::mma(fi[ks], tr_frag(phks(hw), C::RPK, ks * M::KSTEP, 32 * ct, lane), a);
           if (hi == 0) zsum(hw)[32 * ct + l32] = a[0];
         }
       }
