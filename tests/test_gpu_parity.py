@@ -359,6 +359,22 @@ def test_chunking_variants(plan, wg1, wg2):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("chunks", [2, 3, 5, 9, 17, 33, 64])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reduce_tree_sizes(plan, chunks, d):
+    """Every size of the reduce kernel's tree (it is unrolled for the power of
+    two at or above the chunk count): pass 1 asked for `chunks` chunks per
+    head on the 480p grid (whole 64-token tiles per chunk give 2, 3, 5, 9, 17,
+    23 and 34, so trees of 2 to 64 leaves), against the oracle."""
+    heads = 2
+    plan("pass1_workgroups", heads * chunks)
+    inp = make_inputs(11, 15, 26, heads, d, "bf16", seed=23)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"{chunks} chunks per head, d={d}", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("shape", [(5, 9, 13, 3, 128), (3, 22, 40, 2, 128), (1, 1, 1, 2, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_generic_pass1_kernel_bf16(plan, shape):
