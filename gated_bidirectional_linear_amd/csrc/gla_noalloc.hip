@@ -10,7 +10,7 @@
 
 namespace {
 // 64 MiB: the 720p/60s workload (159,280 tokens, 32 heads, d = 128) needs
-// 19 MB; any bidirectional call with at most 256 heads at d = 128 and a few
+// 20 MB; any bidirectional call with at most 256 heads at d = 128 and a few
 // hundred thousand frames' RoPE rows fits.  Every device the library runs on
 // holds one copy until the process ends.
 constexpr size_t kScratchBytes = size_t(64) << 20;

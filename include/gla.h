@@ -227,8 +227,10 @@ int gla_token_causal_forward_batch(const void* q, const void* k, const void* v, 
  * before anything is enqueued.  The need is about
  *     (T*d/8 + (H + W)*3d/16)*8 + (P + 1)*heads*(d*d + d)*4 bytes,
  * with P <= 64 chunk partials per head (about max(1, 256/heads) at d = 128 in
- * bf16 or fp8, max(1, 512/heads) otherwise): the 720p/60s workload
- * (159,280 tokens, 32 heads, d = 128) needs 19 MB.
+ * bf16 or fp8, max(1, 512/heads) otherwise), plus heads*d*d*2 bytes for the
+ * bf16 copy of the states when the four-head output kernel runs (d = 128,
+ * bf16 or fp8, heads divisible by 4): the 720p/60s workload (159,280 tokens,
+ * 32 heads, d = 128) needs 20 MB.
  *
  * Concurrency: every call on one device uses that device's one array.  Calls
  * that can overlap on a device (on different streams, or from different
