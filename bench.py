@@ -427,6 +427,14 @@ def main(argv=None):
         print(f"bench.py runs on one GPU only: this operator's path is measured per GPU "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         return 2
+    from gated_bidirectional_linear_amd import PLAN_KNOBS
+    plan = {}
+    for kv in args.plan:
+        name, _, value = kv.partition("=")
+        if name not in PLAN_KNOBS or not value.isdigit():
+            print(f"--plan {kv}: expected KNOB=VALUE with KNOB in {sorted(PLAN_KNOBS)}", file=sys.stderr)
+            return 2
+        plan[name] = int(value)
 
     import numpy as np
     import torch
@@ -437,14 +445,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    plan = {}
-    for kv in args.plan:
-        name, _, value = kv.partition("=")
-        if name not in gla.PLAN_KNOBS or not value.isdigit():
-            print(f"--plan {kv}: expected KNOB=VALUE with KNOB in {sorted(gla.PLAN_KNOBS)}", file=sys.stderr)
-            return 2
-        gla.plan_override(name, int(value))
-        plan[name] = int(value)
+    for name, value in plan.items():
+        gla.plan_override(name, value)
     w = WORKLOADS[args.workload]
     B = args.batch
     if B < 1:
