@@ -28,14 +28,17 @@ def _graph_replays(fn, out, eager_ref, reps=3):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), eager_ref.view(torch.int16)), f"replay {r} differs"
+        bits = torch.int16 if out.element_size() == 2 else (torch.uint8 if out.element_size() == 1 else torch.int32)
+        assert torch.equal(out.view(bits), eager_ref.view(bits)), f"replay {r} differs"
         _ = (eager_ref.float() * 2).sum().item()   # eager work between replays
 
 
-def test_forward_graph_replay():
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "e5m2"])
+def test_forward_graph_replay(dtype):
+    """Four heads at d = 128: the four-head output kernel (bf16 or fp8 rows)."""
     torch = pytest.importorskip("torch")
     import gated_bidirectional_linear_amd as gla
-    inp = make_inputs(4, 9, 10, 4, 128, "bf16", seed=51)
+    inp = make_inputs(4, 9, 10, 4, 128, dtype, seed=51)
     dev = to_device(inp)
     ref = gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"], eps=inp["eps"])
     torch.cuda.synchronize()
