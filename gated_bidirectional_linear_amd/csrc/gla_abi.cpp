@@ -512,7 +512,7 @@ const char* gla_status_string(int status) {
   }
 }
 
-int gla_version(void) { return (1 << 16) | 5; }
+int gla_version(void) { return (1 << 16) | 6; }
 
 int gla_timing_enable(int on) {
   EventTimer& tm = timer();

@@ -245,7 +245,7 @@ int gla_forward_noalloc(const void* q, const void* k, const void* v, const void*
 /* Static text for a gla_status value (never NULL). */
 const char* gla_status_string(int status);
 
-/* Library ABI version: (major << 16) | minor. */
+/* Library ABI version: (major << 16) | minor.  Minor 6: GLA_DTYPE_FP8_E5M2. */
 int gla_version(void);
 
 /*

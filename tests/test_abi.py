@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert lib.gla_version() >> 16 == 1
-    assert lib.gla_version() & 0xFFFF >= 5   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal;
-    #                                          1.4: batches; 1.5: gla_forward_noalloc
+    assert lib.gla_version() & 0xFFFF >= 6   # 1.1: gla_block_causal_forward_at; 1.2: fp8 e4m3 I/O; 1.3: token-causal;
+    #                                          1.4: batches; 1.5: gla_forward_noalloc; 1.6: fp8 e5m2 I/O
     for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_HIP, E_ALLOC, E_D, E_ALIAS, E_TOO_LARGE):
         s = lib.gla_status_string(st).decode()
         assert s and s != "unknown status"
