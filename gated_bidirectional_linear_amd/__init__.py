@@ -40,6 +40,8 @@ __all__ = [
     "timing_select",
     "plan_override",
     "plan_reset",
+    "plan_describe",
+    "PLAN_FIELDS",
     "PLAN_KNOBS",
     "DTYPE_F32",
     "DTYPE_BF16",
@@ -233,6 +235,24 @@ def plan_override(knob: str, value: int) -> None:
     st = load().gla_plan_override(PLAN_KNOBS[knob], int(value))
     if st != 0:
         raise GlaError(st, "gla_plan_override")
+
+
+PLAN_FIELDS = ("seg_len", "segs_item", "cps1", "chunk1", "cps2", "chunk2", "pass1_reg", "pass2_heads", "rope_lds1",
+               "rope_lds2")
+_FORMS = {"bidirectional": 0, "block_causal": 1, "token_causal": 2}
+
+
+def plan_describe(form: str, grid, heads: int, d: int, dtype: int, batch: int = 1, block_frames: int = 1) -> dict:
+    """The launch plan a call with these shapes would use under the current
+    knobs (PLAN_FIELDS; pass2_heads 0 means one head per workgroup).  For
+    tests; needs no device."""
+    T, H, W = (int(x) for x in grid)
+    out = (ctypes.c_int * len(PLAN_FIELDS))()
+    st = load().gla_plan_describe(_FORMS[form], int(batch), T, H, W, int(heads), int(d), int(dtype),
+                                  int(block_frames), out, len(PLAN_FIELDS))
+    if st != 0:
+        raise GlaError(st, "gla_plan_describe")
+    return dict(zip(PLAN_FIELDS, out))
 
 
 def plan_reset() -> None:

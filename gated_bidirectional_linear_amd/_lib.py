@@ -37,6 +37,7 @@ SIGNATURES = {
     "gla_kernel_name": (ctypes.c_char_p, [_i]),
     "gla_timing_select": (_i, [ctypes.c_uint]),
     "gla_plan_override": (_i, [_i, _i]),
+    "gla_plan_describe": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_i), _i]),
 }
 
 _LIB = None

@@ -126,7 +126,12 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
     return yx + frames * (d / 8) <= entries;
   };
 
-  G.pass1_reg = (narrow && d == 128 && !kn.on(GLA_PLAN_PASS1_GENERIC)) ? 1 : 0;
+  // Whether any chunk's RoPE rows fit in LDS (the y and x blocks plus one
+  // frame).  Where they cannot, every kernel reads the global table, and
+  // smaller chunks would buy nothing.
+  const bool lds_any = !kn.on(GLA_PLAN_ROPE_GLOBAL) && rope_fits(1);
+
+  G.pass1_reg = (narrow && d == 128 && lds_any && !kn.on(GLA_PLAN_PASS1_GENERIC)) ? 1 : 0;
   const int target1 = G.pass1_reg ? kDefaultTargetWgAcc1 : kDefaultTargetWg1;
   // the register-accumulating kernel runs one workgroup per CU: rounding the
   // chunk count down keeps the launch to one round of workgroups (20 heads:
@@ -137,7 +142,8 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
   // more (smaller) chunks when a chunk's RoPE rows would not fit in LDS
-  while (!rope_fits((long)ceil_div(tiles_per_seg, cps1) * kTile) && cps1 < gla::kMaxChunks && cps1 < tiles_per_seg)
+  while (lds_any && !rope_fits((long)ceil_div(tiles_per_seg, cps1) * kTile) && cps1 < gla::kMaxChunks &&
+         cps1 < tiles_per_seg)
     ++cps1;
   G.chunk1 = ceil_div(tiles_per_seg, cps1) * kTile;
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
@@ -151,7 +157,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // for the one-head kernel, and the whole call 825-836 us against 840-853 us.
   const int max_hp = kn.on(GLA_PLAN_PASS2_GENERIC) ? 1 : kn.get(GLA_PLAN_PASS2_HEADS, 4);
   G.pass2_pair = 0;
-  if (narrow && d == 128 && !token_causal) {   // bf16 or fp8 I/O
+  if (narrow && d == 128 && !token_causal && lds_any) {   // bf16 or fp8 I/O
     if (heads % 4 == 0 && max_hp >= 4) G.pass2_pair = 4;
     else if (bf16_io && heads % 2 == 0 && max_hp >= 2) G.pass2_pair = 2;
   }
@@ -179,7 +185,7 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   const int units_per_seg2 = ceil_div(G.seg_len, unit2);
   int cps2 = want2 < 1 ? 1 : want2;
   if (cps2 > units_per_seg2) cps2 = units_per_seg2;
-  while (!rope_fits((long)ceil_div(units_per_seg2, cps2) * unit2) && cps2 < units_per_seg2) ++cps2;
+  while (lds_any && !rope_fits((long)ceil_div(units_per_seg2, cps2) * unit2) && cps2 < units_per_seg2) ++cps2;
   G.chunk2 = ceil_div(units_per_seg2, cps2) * unit2;
   G.cps2 = ceil_div(G.seg_len, G.chunk2);
   G.rope_lds2 = rope_fits(G.chunk2) ? 1 : 0;
@@ -547,6 +553,27 @@ int gla_timing_select(unsigned mask) {
   EventTimer& tm = timer();
   std::lock_guard<std::mutex> lk(tm.mu);
   tm.mask = mask;
+  return GLA_OK;
+}
+
+int gla_plan_describe(int form, int batch, int T, int H, int W, int heads, int d, int dtype, int block_frames,
+                      int* out, int n) {
+  if (form < 0 || form > 2) return GLA_ERR_SHAPE;
+  const Form f = form == 0 ? Form::bidirectional : (form == 1 ? Form::block_causal : Form::token_causal);
+  // shape checks of the operator calls, without the tensors
+  const int st = validate(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, T, H, W, heads, d, 1e-6f, nullptr,
+                          dtype, f != Form::bidirectional, nullptr, nullptr,
+                          f == Form::block_causal ? block_frames : 1, batch);
+  if (st != GLA_OK && st != GLA_ERR_NULL) return st;
+  if ((long long)T * H * W == 0) return GLA_ERR_SHAPE;   // an empty grid has no plan
+  if (out == nullptr && n > 0) return GLA_ERR_NULL;
+  const Knobs kn = Knobs::snapshot();
+  const int seg_len = segment_length(f, T, H, W, heads, block_frames, batch, kn);
+  const Geometry G = plan(T, H, W, heads, d, 1e-6f, seg_len, f == Form::token_causal, elem_size(dtype) <= 2,
+                          dtype == GLA_DTYPE_BF16, batch, kn);
+  const int v[] = {G.seg_len, G.segs_item, G.cps1, G.chunk1, G.cps2, G.chunk2,
+                   G.pass1_reg, G.pass2_pair, G.rope_lds1, G.rope_lds2};
+  for (int i = 0; i < n && i < (int)(sizeof(v) / sizeof(v[0])); ++i) out[i] = v[i];
   return GLA_OK;
 }
 

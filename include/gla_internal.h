@@ -46,6 +46,22 @@ typedef enum {
  */
 int gla_plan_override(int knob, int value);
 
+/*
+ * The launch plan that a call with these shapes would use under the current
+ * knobs, for tests: writes the first n of {tokens per segment, segments per
+ * batch item, pass-1 chunks per segment, pass-1 tokens per chunk, pass-2
+ * chunks per segment, pass-2 tokens per chunk, register-accumulating pass 1
+ * (0 or 1), heads per pass-2 workgroup (0 for one head, 2 or 4), pass-1 RoPE
+ * rows in LDS (0 or 1), pass-2 RoPE rows in LDS (0 or 1)} to out.  form: 0
+ * bidirectional, 1 block-causal (block_frames frames per block), 2
+ * token-causal.  Returns GLA_OK, or the status the operator call would return
+ * for these shapes, dtype and head dim (GLA_ERR_SHAPE also for an empty grid
+ * or an unknown form; GLA_ERR_NULL for out == NULL with n > 0).  Touches no
+ * device.
+ */
+int gla_plan_describe(int form, int batch, int T, int H, int W, int heads, int d, int dtype, int block_frames,
+                      int* out, int n);
+
 #ifdef __cplusplus
 }
 #endif
