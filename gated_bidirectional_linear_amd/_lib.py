@@ -47,8 +47,25 @@ class LibraryNotBuilt(RuntimeError):
     pass
 
 
+def hip_runtimes() -> list:
+    """Files of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load (once) and return the HIP library; raise if it is missing."""
+    """Load (once) and return the HIP library; raise if it is missing.
+
+    The library must share the HIP runtime of the process's PyTorch, which
+    owns the device memory and streams it is handed.  PyTorch ships its own
+    copy of the runtime; importing it first lets the dynamic linker satisfy
+    the library's runtime dependency with that copy.  Loaded the other way
+    round, a second runtime (with its own HSA runtime) would come in beside
+    it, and PyTorch's streams would be foreign to the library.  A process
+    that already holds two runtimes is refused."""
     global _LIB
     if _LIB is not None:
         return _LIB
@@ -56,7 +73,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise LibraryNotBuilt(
             f"{path} is missing: build it with `python -m gated_bidirectional_linear_amd.build` "
             "(hipcc, gfx950). There is no CPU fallback.")
+    import torch  # noqa: F401  (binds the library to PyTorch's HIP runtime)
     lib = ctypes.CDLL(path)
+    runtimes = hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError("more than one HIP runtime is loaded in this process (" + ", ".join(runtimes) +
+                           "): load PyTorch before any other HIP library")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -5,6 +5,7 @@ import ctypes
 import math
 import os
 import re
+import sys
 
 import pytest
 
@@ -310,3 +311,34 @@ def test_noalloc_validation_and_size_limit(lib):
     assert fna(lib, T=600_000, H=1, W=1, heads=1, d=128) == E_TOO_LARGE
     # 1,024 heads at d = 128: at least 2 * 1,024 states of 66 KB
     assert fna(lib, T=2, H=4, W=4, heads=1024, d=128) == E_TOO_LARGE
+
+
+def _run(code):
+    import subprocess
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loaded before anything imports torch (as a first knob call does), the
+    library still binds to PyTorch's HIP runtime: one runtime in the process."""
+    r = _run("import gated_bidirectional_linear_amd as gla, gated_bidirectional_linear_amd._lib as L\n"
+             "gla.plan_override('pass2_heads', 0)\n"
+             "import torch\n"
+             "print(len(L.hip_runtimes()))")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_second_hip_runtime_is_refused():
+    """A process that already mapped another copy of the HIP runtime is
+    refused with an error rather than left to mix two runtimes."""
+    import glob
+    import torch
+    others = [p for p in glob.glob("/opt/rocm*/lib/libamdhip64.so*") if os.path.isfile(p)]
+    if not others or os.path.dirname(torch.__file__) in others[0]:
+        pytest.skip("no second HIP runtime on this machine")
+    r = _run(f"import ctypes; ctypes.CDLL({others[0]!r})\n"
+             "import gated_bidirectional_linear_amd._lib as L\n"
+             "try:\n    L.load()\nexcept RuntimeError as e:\n    print('refused', e)\n")
+    assert r.returncode == 0, r.stderr
+    assert "refused" in r.stdout and "more than one HIP runtime" in r.stdout
