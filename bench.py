@@ -31,7 +31,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "e5m2": 2500.0, "f32": 157.3}
 # the kernels use (fp8 I/O of either format is widened to bf16 operands; fp32 I/O runs fp32 MFMA)
 METRIC = "tokens/s + achieved HBM GB/s (% of peak), gated linear attn fwd, 720p/60s grid"
 KERNEL_SOURCES = ["gated_bidirectional_linear_amd/csrc/" + f for f in
-                  ("gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip", "gla_output.hip")]
+                  ("gla_launch.h", "gla_device.h", "gla_common.h", "gla_tables.hip", "gla_state.hip",
+                   "gla_output.hip")]
 CAUSAL_SOURCES = KERNEL_SOURCES + ["gated_bidirectional_linear_amd/csrc/gla_causal.hip"]
 
 

@@ -120,10 +120,10 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   // frames it can span (at worst alignment).
   const int HW = H * W;
   const long yx = (long)H * (3 * d / 16) + (long)W * (3 * d / 16);
-  auto rope_fits = [&](long L, int entries = gla::kRopeLdsEntries) {
+  auto rope_fits = [&](long L, int entries = gla::kRopeLdsEntries, long max_frames = 1L << 30) {
     long frames = (L + HW - 2) / HW + 1;
     if (frames > T) frames = T;
-    return yx + frames * (d / 8) <= entries;
+    return frames <= max_frames && yx + frames * (d / 8) <= entries;
   };
 
   // Whether any chunk's RoPE rows fit in LDS (the y and x blocks plus one
@@ -142,12 +142,13 @@ Geometry plan(int T, int H, int W, int heads, int d, float eps, int seg_len, boo
   if (cps1 > gla::kMaxChunks) cps1 = gla::kMaxChunks;
   if (cps1 > tiles_per_seg) cps1 = tiles_per_seg;
   // more (smaller) chunks when a chunk's RoPE rows would not fit in LDS
-  while (lds_any && !rope_fits((long)ceil_div(tiles_per_seg, cps1) * kTile) && cps1 < gla::kMaxChunks &&
-         cps1 < tiles_per_seg)
+  const long frames1 = G.pass1_reg ? gla::kRegRopeMaxFrames : 1L << 30;
+  while (lds_any && !rope_fits((long)ceil_div(tiles_per_seg, cps1) * kTile, gla::kRopeLdsEntries, frames1) &&
+         cps1 < gla::kMaxChunks && cps1 < tiles_per_seg)
     ++cps1;
   G.chunk1 = ceil_div(tiles_per_seg, cps1) * kTile;
   G.cps1 = ceil_div(G.seg_len, G.chunk1);
-  G.rope_lds1 = rope_fits(G.chunk1) ? 1 : 0;
+  G.rope_lds1 = rope_fits(G.chunk1, gla::kRopeLdsEntries, frames1) ? 1 : 0;
 
   // Heads per workgroup of pass 2 at d = 128: four where the head count allows
   // (bf16: 1 KB token row segments; fp8: 512 bytes), else pairs for bf16 (the

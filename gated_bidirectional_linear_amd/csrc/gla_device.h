@@ -396,26 +396,29 @@ struct Rope {
 
   // Copy the frames [t_lo, t_lo + nt) and the y/x blocks of the global table
   // into LDS (all kThreads threads take part; caller synchronises).  At most
-  // kMaxEntries entries; every thread issues its loads together (indices
-  // past the end are clamped to entry 0 and not stored).
+  // kMaxEntries entries, in rounds of 8 per thread: every thread issues a
+  // round's loads together (indices past the end are clamped to entry 0 and
+  // not stored).
   template <int kMaxEntries>
   __device__ __forceinline__ static View stage(float2* lds, const float2* __restrict__ tab, int T, int H, int W,
                                                int t_lo, int nt) {
-    constexpr int PER = kMaxEntries / kThreads;
-    static_assert(kMaxEntries % kThreads == 0, "staging split");
+    constexpr int PER = 8;
     const int n_t = nt * PT;
     const int total = n_t + H * PY + W * PX;
-    float2 tmp[PER];
+    const int lim = total < kMaxEntries ? total : kMaxEntries;
+    for (int base = 0; base < lim; base += PER * kThreads) {
+      float2 tmp[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = (int)threadIdx.x + j * kThreads;
-      const int src = (i < n_t) ? t_lo * PT + i : T * PT + (i - n_t);
-      tmp[j] = tab[i < total ? src : 0];
-    }
+      for (int j = 0; j < PER; ++j) {
+        const int i = base + (int)threadIdx.x + j * kThreads;
+        const int src = (i < n_t) ? t_lo * PT + i : T * PT + (i - n_t);
+        tmp[j] = tab[i < lim ? src : 0];
+      }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = (int)threadIdx.x + j * kThreads;
-      if (i < total) lds[i] = tmp[j];
+      for (int j = 0; j < PER; ++j) {
+        const int i = base + (int)threadIdx.x + j * kThreads;
+        if (i < lim) lds[i] = tmp[j];
+      }
     }
     return View{lds, t_lo, nt, H};
   }

@@ -35,7 +35,12 @@ namespace gla {
 
 constexpr int kMaxChunks = 64;   // chunk partials per segment reduced by one tree
 constexpr int kNumKernels = 4;   // rope table, state partials, reduce/prefix, output
-constexpr int kRopeLdsEntries = 2048;  // float2 entries of RoPE table a workgroup may stage in LDS (16 KB)
+// float2 entries of RoPE table a workgroup may stage in LDS (24 KB): at d = 128
+// the y and x blocks of a 34 x 60 latent frame (1080p) and some 40 frames
+constexpr int kRopeLdsEntries = 3072;
+// Frames a chunk of the register-accumulating pass-1 kernel may span: its
+// packed table row offsets give the frame rows 10 bits of 16-byte units.
+constexpr int kRegRopeMaxFrames = 128;
 // The token-causal kernel stages fewer (14 KB) so that two workgroups fit on a CU.
 constexpr int kRopeLdsEntriesCausal = 1792;
 

@@ -249,7 +249,16 @@ __global__ __launch_bounds__(kThreads) void state_partial_kernel(
 namespace frag1 {
 constexpr int D = 128;
 constexpr int kStep = 16;    // tokens per step (one MFMA K)
-constexpr int kOffBits = 10;                   // packed table row offset (16-byte units)
+// Packed table row offsets (16-byte units) of a token, one word for its three
+// axes.  A table of at most kNarrowEntries entries takes 10-bit fields (frame,
+// y and x rows at bits 0, 10 and 20); a wide one (up to kRopeLdsEntries) 11-bit
+// y and x fields at bits 10 and 21 beside the 10-bit frame field (a chunk spans
+// at most kRegRopeMaxFrames frames).  The kernel is instantiated for both.
+constexpr int kNarrowEntries = 2048;
+template <bool WIDE> struct Pack {
+  static constexpr int TB = 10, YB = WIDE ? 11 : 10, XB = WIDE ? 11 : 10;
+  static constexpr int kEntries = WIDE ? kRopeLdsEntries : kNarrowEntries;
+};
 constexpr int kRotBytes = kRopeLdsEntries * 8; // LDS rotation table
 using R = Rope<D>;
 
@@ -317,11 +326,13 @@ struct Lane {
   uint32_t ROW;             // bytes between tokens
   uint32_t lane_rel;        // this lane's pair offset inside a table row (16-byte units)
   uint32_t ashift;          // bit offset of this lane's axis in the packed row offsets
+  uint32_t awidth;          // and its width (wide tables)
   int t_lo, t_last, nt;     // frames the chunk spans
 };
 
-template <typename E>
+template <typename E, bool WIDE>
 __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
+  using P = Pack<WIDE>;
   constexpr uint32_t ES = Io<E>::ES;
   Lane L;
   L.lane = threadIdx.x & 63;
@@ -334,7 +345,13 @@ __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
   const int axis = (2 * L.m < R::PT) ? 0 : ((2 * L.m < R::PT + R::PY) ? 1 : 2);
   const int first = axis == 0 ? 0 : (axis == 1 ? R::PT : R::PT + R::PY);
   L.lane_rel = (uint32_t)(2 * L.m - first) / 2;
-  L.ashift = (uint32_t)axis * kOffBits;
+  if constexpr (WIDE) {
+    L.ashift = axis == 0 ? 0u : (axis == 1 ? (uint32_t)P::TB : (uint32_t)(P::TB + P::YB));
+    L.awidth = axis == 0 ? (uint32_t)P::TB : (uint32_t)P::YB;
+  } else {
+    L.ashift = (uint32_t)axis * P::TB;
+    L.awidth = (uint32_t)P::TB;
+  }
   const int HW = G.H * G.W;
   L.t_lo = ch.begin < ch.end ? (int)(ch.begin / HW) : 0;
   L.t_last = ch.begin < ch.end ? (int)((ch.end - 1) / HW) : 0;
@@ -346,9 +363,10 @@ __device__ __forceinline__ Lane make_lane(const Geometry& G, const Chunk& ch) {
 // computed into LDS as per-pair bf16 words (cos, -sin), (sin, cos), and
 // written in fp32 to the global table for the later kernels (the y/x blocks
 // by one workgroup).  All threads take part; the caller synchronises.
+template <bool WIDE>
 __device__ __forceinline__ void compute_rotations(unsigned char* rtab, double* freq, float2* __restrict__ rope,
                                                   const Geometry& G, const Lane& L, bool write_yx) {
-  R::template compute<kRopeLdsEntries, kThreads>(
+  R::template compute<Pack<WIDE>::kEntries, kThreads>(
       [&](int e, float2 cs) {
         *reinterpret_cast<u32x2*>(rtab + 8 * e) = (u32x2){pack2bf(cs.x, -cs.y), pack2bf(cs.y, cs.x)};
       },
@@ -384,12 +402,18 @@ __device__ __forceinline__ void issue(Rows<E>& r, const E* __restrict__ k, const
 }
 
 // Table row offsets (16-byte units) of the token at `gp` on the three axes.
+template <bool WIDE>
 __device__ __forceinline__ uint32_t table_rows(const GridPos& gp, const Lane& L, int H) {
+  using P = Pack<WIDE>;
   const int tc = gp.t < L.t_last ? gp.t : L.t_last;
   return (uint32_t)((tc - L.t_lo) * R::PT / 2) |
-         ((uint32_t)((L.nt * R::PT + gp.y * R::PY) / 2) << kOffBits) |
-         ((uint32_t)((L.nt * R::PT + H * R::PY + gp.x * R::PX) / 2) << (2 * kOffBits));
+         ((uint32_t)((L.nt * R::PT + gp.y * R::PY) / 2) << P::TB) |
+         ((uint32_t)((L.nt * R::PT + H * R::PY + gp.x * R::PX) / 2) << (P::TB + P::YB));
 }
+static_assert(Pack<true>::TB + Pack<true>::YB + Pack<true>::XB == 32, "three fields in one word");
+static_assert(Pack<false>::kEntries / 2 <= (1 << Pack<false>::XB), "narrow: rows fit 10-bit fields");
+static_assert(Pack<true>::kEntries / 2 <= (1 << Pack<true>::XB), "wide: y and x rows fit 11-bit fields");
+static_assert((kRegRopeMaxFrames - 1) * R::PT / 2 < (1 << Pack<true>::TB), "frame rows fit their field");
 
 // Lane l "owns" token 8h + (l & 7) of a step: every 16-lane row holds the 8
 // tokens of its half, so DPP row_newbcast:i hands token i of the lane's half
@@ -410,7 +434,7 @@ __device__ __forceinline__ int row_bcast(int x) {
 struct NoWork {
   __device__ __forceinline__ void operator()(int) const {}
 };
-template <typename E, typename Between = NoWork>
+template <typename E, bool WIDE, typename Between = NoWork>
 __device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, const unsigned char* rtab, const Lane& L,
                                            float eps, float (&zacc)[4], u32x4 (&kf)[4], u32x4 (&vf)[4],
                                            Between between = Between()) {
@@ -426,7 +450,7 @@ __device__ __forceinline__ void build_step(const Rows<E>& raw, uint32_t offs, co
 #define GLA_FETCH(I)                                                                                 \
   {                                                                                                  \
     const uint32_t o = (uint32_t)row_bcast<I>((int)offs);                                            \
-    cs[I] = *reinterpret_cast<const u32x4*>(rtab + 16 * (__builtin_amdgcn_ubfe(o, L.ashift, kOffBits) + L.lane_rel)); \
+    cs[I] = *reinterpret_cast<const u32x4*>(rtab + 16 * (__builtin_amdgcn_ubfe(o, L.ashift, WIDE ? L.awidth : (uint32_t)Pack<false>::TB) + L.lane_rel)); \
   }
   GLA_FETCH(0) GLA_FETCH(1) GLA_FETCH(2) GLA_FETCH(3) GLA_FETCH(4) GLA_FETCH(5) GLA_FETCH(6) GLA_FETCH(7)
 #undef GLA_FETCH
@@ -532,13 +556,14 @@ __device__ __forceinline__ void write_key_sum(float (&zacc)[4], float* zred, flo
 namespace acc1 {
 constexpr int kHalfBytes = 32 * 1024;        // half of one wave's state (v-side slots 2R, 2R + 1)
 constexpr int kSumBytes = 4 * kHalfBytes;    // the 4 waves' halves during the final sum
+static_assert(frag1::kRotBytes <= kSumBytes, "the rotation table lies inside the final-sum space");
 #ifndef GLA_ACC_DEPTH
 #define GLA_ACC_DEPTH 3
 #endif
 constexpr int kDepth = GLA_ACC_DEPTH;        // steps of rows in flight per wave
 }  // namespace acc1
 
-template <typename E>
+template <typename E, bool WIDE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_partial_acc_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const E* __restrict__ beta,
     float2* __restrict__ rope, float* __restrict__ partial, Geometry G) {
@@ -552,13 +577,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int lin = xcd_swizzle(blockIdx.x, gridDim.x);
   const Chunk ch = chunk_of(lin, G, G.cps1, G.chunk1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const Lane L = make_lane<E>(G, ch);
+  const Lane L = make_lane<E, WIDE>(G, ch);
   const int HW = G.H * G.W;
   // the first rows are requested before the RoPE rows are computed
   Rows<E> rr[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(rr[d], k, v, beta, ch.begin + d * kTile + wave * kStep, ch.end, G.heads, L);
-  compute_rotations(rtab, reinterpret_cast<double*>(zred), rope, G, L, lin == 0);
+  compute_rotations<WIDE>(rtab, reinterpret_cast<double*>(zred), rope, G, L, lin == 0);
 
   // grid position of this lane's own token; a wave's steps are 64 apart
   GridPos gp;
@@ -595,7 +620,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // on every path the compiler waits for exactly the rows a step uses.
   auto step = [&](Rows<E>& rows, long t0) {
     u32x4 kf[4], vf[4];
-    build_step(rows, table_rows(gp, L, G.H), rtab, L, G.eps, zacc, kf, vf, mfma_row);
+    build_step<E, WIDE>(rows, table_rows<WIDE>(gp, L, G.H), rtab, L, G.eps, zacc, kf, vf, mfma_row);
     gp.advance(adt, ady, adx, G.H, G.W);
     issue(rows, k, v, beta, t0 + kDepth * kTile + wave * kStep, ch.end, G.heads, L);
 #pragma unroll
@@ -651,8 +676,17 @@ hipError_t launch_state_partial(const LaunchArgs& a) {
   const int blocks = G.heads * G.nseg * G.cps1;
   if constexpr (D == 128 && Elem<typename Elem<E>::Lds>::is_bf16) {   // bf16 and fp8 rows
     if (G.pass1_reg) {   // the planner sets it only with the RoPE rows in LDS
-      hipLaunchKernelGGL((state_partial_acc_kernel<E>), dim3(blocks), dim3(kThreads), 0, a.stream, (const E*)a.k,
-                         (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
+      // entries of the table a chunk stages: the y and x blocks and the frames it spans
+      const long HW = (long)G.H * G.W;
+      long frames = (G.chunk1 + HW - 2) / HW + 1;
+      if (frames > G.T_item) frames = G.T_item;
+      const long entries = (long)(G.H + G.W) * (3 * D / 16) + frames * (D / 8);
+      if (entries > frag1::kNarrowEntries)
+        hipLaunchKernelGGL((state_partial_acc_kernel<E, true>), dim3(blocks), dim3(kThreads), 0, a.stream,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
+      else
+        hipLaunchKernelGGL((state_partial_acc_kernel<E, false>), dim3(blocks), dim3(kThreads), 0, a.stream,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.beta, a.rope, a.partial, G);
       return hipGetLastError();
     }
   }

@@ -185,3 +185,19 @@ def test_fp8_block_causal_four_heads(plan):
     _report(f"block-causal four heads {(T, H, W, heads, F)}", err)
     assert err <= TOL["fp8"]
     assert rel_err(to_f64(z), rz) <= Z_TOL["fp8"]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "e5m2"])
+def test_fp8_wide_frame_rope_rows_in_lds(fmt):
+    """34 x 60 latent frames (1080p): y and x RoPE blocks of 2,256 entries
+    staged in LDS for the register pass 1 and the four-head output kernel."""
+    import gated_bidirectional_linear_amd as gla
+    code = gla.DTYPE_FP8_E4M3 if fmt == "fp8" else gla.DTYPE_FP8_E5M2
+    p = gla.plan_describe("bidirectional", (3, 34, 60), 4, 128, code)
+    assert (p["rope_lds1"], p["rope_lds2"], p["pass1_reg"], p["pass2_heads"]) == (1, 1, 1, 4)
+    inp = make_inputs(3, 34, 60, 4, 128, fmt, seed=45)
+    got = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = fp8_excess(got, _oracle(inp), fmt)
+    _report(f"wide frame {fmt}", err)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[fmt]

@@ -82,6 +82,26 @@ def test_long_sequence_workload_full():
     assert err <= TOL["bf16"]
 
 
+def test_1080p_workload_full():
+    """The 1080p/121-frame latent grid (31 x 34 x 60, N = 63,240, 32 heads) at
+    full size in the default plan: its y and x RoPE blocks (2,256 entries at
+    d = 128) are staged in LDS beside the chunk's frames, so the register
+    pass 1 and the four-head output kernel run.  Every output of every head
+    against the oracle, 8 heads per oracle call."""
+    import gated_bidirectional_linear_amd as gla
+    w = WORKLOADS["1080p_121f"]
+    p = gla.plan_describe("bidirectional", (w.T, w.H, w.W), w.heads, w.d, gla.DTYPE_BF16)
+    assert (p["rope_lds1"], p["rope_lds2"], p["pass1_reg"], p["pass2_heads"]) == (1, 1, 1, 4)
+    print(f"[case] {w.name} N={w.N} heads={w.heads}", flush=True)
+    inp = make_workload_inputs(w, seed=0, keep_f32=False)
+    dev = to_device(inp)
+    out = run_forward(dev, inp["grid"], inp["eps"])
+    del dev
+    err = grouped_head_error(out, inp, lambda sub: _oracle(sub), label=w.name)
+    _report(w.name + " all heads, all rows", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # Shapes: head dims, ragged token counts, tiny grids
 # ---------------------------------------------------------------------------
@@ -345,6 +365,40 @@ def test_large_frame_grid_falls_back_to_global_table():
     out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
     err = rel_err(out, _oracle(inp))
     _report("64x64 frame", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("grid", [(3, 34, 60), (2, 40, 80)], ids=lambda g: "x".join(map(str, g)))
+def test_wide_frame_rope_rows_in_lds(grid, dtype):
+    """Frames of 34 x 60 and 40 x 80 latent pixels: y and x RoPE blocks of
+    2,256 and 2,880 entries at d = 128, more than 2,048, staged in LDS in more
+    than one round; bf16 runs the register pass 1 and the four-head output
+    kernel on them."""
+    import gated_bidirectional_linear_amd as gla
+    T, H, W = grid
+    code = gla.DTYPE_F32 if dtype == "f32" else gla.DTYPE_BF16
+    p = gla.plan_describe("bidirectional", grid, 4, 128, code)
+    assert (p["rope_lds1"], p["rope_lds2"]) == (1, 1)
+    if dtype == "bf16":
+        assert (p["pass1_reg"], p["pass2_heads"]) == (1, 4)
+    inp = make_inputs(T, H, W, 4, 128, dtype, seed=19)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report(f"wide frame {grid} {dtype}", err, TOL[dtype])
+    assert err <= TOL[dtype]
+
+
+def test_pass1_chunk_spanning_128_frames():
+    """One latent pixel per frame, 8,192 frames: each register pass-1 chunk
+    spans 128 frames, the most its packed frame-row offsets address."""
+    import gated_bidirectional_linear_amd as gla
+    p = gla.plan_describe("bidirectional", (8192, 1, 1), 4, 128, gla.DTYPE_BF16)
+    assert (p["pass1_reg"], p["rope_lds1"], p["chunk1"]) == (1, 1, 128)
+    inp = make_inputs(8192, 1, 1, 4, 128, "bf16", seed=20)
+    out = to_f64(run_forward(to_device(inp), inp["grid"], inp["eps"]))
+    err = rel_err(out, _oracle(inp))
+    _report("128 frames per pass-1 chunk", err, TOL["bf16"])
     assert err <= TOL["bf16"]
 
 

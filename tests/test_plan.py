@@ -18,6 +18,7 @@ TILE = 64
 QUAD_TILE = 16
 TOKEN_TILE = 32
 QUAD_SLOTS = 256
+ROPE_LDS_ENTRIES = 3072
 
 
 def _ceil(a, b):
@@ -56,7 +57,9 @@ def _check(form, grid, heads, d, dtype, batch=1, block_frames=1, default=True):
             assert narrow and d == 128 and heads % 4 == 0 and p["rope_lds2"] == 1
             assert p["chunk2"] % QUAD_TILE == 0
             units = heads // 4 * p["segs_item"] * batch
-            if default:   # one round of workgroups, one per CU
+            # one round of workgroups, one per CU, unless chunks had to be cut
+            # further to fit their RoPE rows in LDS
+            if default and (H + W) * 3 * d // 16 + T * d // 8 <= ROPE_LDS_ENTRIES:
                 assert units * p["cps2"] <= max(QUAD_SLOTS, units)
         else:
             assert p["chunk2"] % TILE == 0
@@ -99,6 +102,19 @@ def test_workload_plans():
     w = WORKLOADS["720p_5s_h20"]
     p = _check("bidirectional", (w.T, w.H, w.W), w.heads, w.d, gla.DTYPE_BF16)
     assert (p["cps2"], p["chunk2"], p["pass2_heads"]) == (44, 320, 4)
+    # 1080p/121 frames: the y and x RoPE blocks (2,256 entries) fit in LDS
+    # beside the chunk's frames, so the register pass 1 and the four-head
+    # output kernel run, one round of 256 workgroups each
+    w = WORKLOADS["1080p_121f"]
+    p = _check("bidirectional", (w.T, w.H, w.W), w.heads, w.d, gla.DTYPE_BF16)
+    assert (p["cps1"], p["chunk1"], p["pass1_reg"], p["rope_lds1"]) == (8, 7936, 1, 1)
+    assert (p["cps2"], p["chunk2"], p["pass2_heads"], p["rope_lds2"]) == (32, 1984, 4, 1)
+    # one pixel per frame: register pass-1 chunks of at most 128 frames (the
+    # reach of its packed frame-row offsets), else the generic kernel
+    p = _check("bidirectional", (8192, 1, 1), 4, 128, gla.DTYPE_BF16)
+    assert (p["pass1_reg"], p["rope_lds1"], p["chunk1"]) == (1, 1, 128)
+    p = _check("bidirectional", (20000, 1, 1), 32, 128, gla.DTYPE_BF16)
+    assert (p["pass1_reg"], p["rope_lds1"]) == (0, 0)
     w = WORKLOADS["block_causal_720p"]
     p = _check("block_causal", (w.T, w.H, w.W), w.heads, w.d, gla.DTYPE_BF16, block_frames=w.block_frames)
     assert (p["seg_len"], p["segs_item"], p["pass2_heads"]) == (3 * 22 * 40, 8, 4)
