@@ -83,7 +83,7 @@ def test_long_sequence_workload_full():
 
 
 def test_1080p_workload_full():
-    """The 1080p/121-frame latent grid (31 x 34 x 60, N = 63,240, 32 heads) at
+    """The 1080p/121-frame latent grid (16 x 34 x 60, N = 32,640, 32 heads) at
     full size in the default plan: its y and x RoPE blocks (2,256 entries at
     d = 128) are staged in LDS beside the chunk's frames, so the register
     pass 1 and the four-head output kernel run.  Every output of every head

@@ -107,8 +107,8 @@ def test_workload_plans():
     # output kernel run, one round of 256 workgroups each
     w = WORKLOADS["1080p_121f"]
     p = _check("bidirectional", (w.T, w.H, w.W), w.heads, w.d, gla.DTYPE_BF16)
-    assert (p["cps1"], p["chunk1"], p["pass1_reg"], p["rope_lds1"]) == (8, 7936, 1, 1)
-    assert (p["cps2"], p["chunk2"], p["pass2_heads"], p["rope_lds2"]) == (32, 1984, 4, 1)
+    assert (p["cps1"], p["chunk1"], p["pass1_reg"], p["rope_lds1"]) == (8, 4096, 1, 1)
+    assert (p["cps2"], p["chunk2"], p["pass2_heads"], p["rope_lds2"]) == (32, 1024, 4, 1)
     # one pixel per frame: register pass-1 chunks of at most 128 frames (the
     # reach of its packed frame-row offsets), else the generic kernel
     p = _check("bidirectional", (8192, 1, 1), 4, 128, gla.DTYPE_BF16)

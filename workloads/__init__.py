@@ -84,7 +84,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("720p_5s_h32", 16, 22, 40, 32, 128, "bf16"),
         Workload("720p_60s", 181, 22, 40, 32, 128, "bf16"),
         Workload("block_causal_720p", 24, 22, 40, 20, 128, "bf16", block_frames=3),
-        Workload("1080p_121f", 31, 34, 60, 32, 128, "bf16"),
+        Workload("1080p_121f", 16, 34, 60, 32, 128, "bf16"),
     ]
 }
 
