@@ -7,8 +7,8 @@ import pytest
 
 import oracle.gla_oracle as orc
 from workloads import WORKLOADS, make_inputs, make_state
-from tests.gpu_helpers import (TOL, Z_TOL, fp8_excess, rel_err, run_block_causal, run_forward, run_token_causal,
-                               to_device, to_f64)
+from tests.gpu_helpers import (FP8_ROUNDING, TOL, Z_TOL, fp8_excess, rel_err, run_block_causal, run_forward,
+                               run_token_causal, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,20 @@ def _err(got, ref, dtype):
     return fp8_excess(got, ref, dtype) if dtype in ("fp8", "e5m2") else rel_err(got, ref)
 
 
+def _agree(got, other, dtype) -> float:
+    """Difference of two GPU outputs of the same item (batched and single
+    calls, whose launch plans may differ) relative to max|other|.  An fp8
+    output is rounded on each side, so the two may sit one output step apart:
+    twice the format's rounding bound (FP8_ROUNDING) is allowed before the
+    path's own difference is counted."""
+    if dtype not in ("fp8", "e5m2"):
+        return rel_err(got, other)
+    rel, ab = FP8_ROUNDING[dtype]
+    ex = np.abs(got - other) - 2.0 * (rel * np.maximum(np.abs(got), np.abs(other)) + ab)
+    den = float(np.max(np.abs(other)))
+    return max(0.0, float(np.max(ex))) / (den if den > 0 else 1.0)
+
+
 def _oracle(it, **kw):
     return orc.gla_forward(it["q"], it["k"], it["v"], it["beta"], it["g"], it["rms_w"], it["grid"], it["eps"], **kw)
 
@@ -45,6 +59,8 @@ SHAPES = [
     (2, 5, 9, 3, 3, 128, "bf16"),
     (3, 3, 4, 5, 2, 128, "fp8"),
     (2, 3, 4, 5, 4, 128, "e5m2"),
+    (2, 2, 34, 60, 4, 128, "bf16"),   # 1080p frames: RoPE tables past 2,048 entries, per item
+    (2, 2, 34, 60, 4, 128, "fp8"),
 ]
 
 
@@ -65,7 +81,7 @@ def test_batch_forward(shape):
         assert np.all(np.isfinite(got))
         assert err <= TOL[dtype]
         single = to_f64(run_forward(devs[b], it["grid"], it["eps"]))
-        assert rel_err(got, single) <= (1e-5 if dtype == "f32" else TOL[dtype])
+        assert _agree(got, single, dtype) <= (1e-5 if dtype == "f32" else TOL[dtype])
 
 
 def test_batch_of_one_is_the_single_call():
