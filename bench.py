@@ -401,6 +401,9 @@ def main(argv=None):
                          "kernel_stats.csv")
     ap.add_argument("--pmc-commands", default="", help="commands recorded in the summaries")
     ap.add_argument("--stats-bench-log", default="", help="output of the profiled bench.py run (its JSON line)")
+    ap.add_argument("--stats-name", default="",
+                    help="name of the kernel-trace summary (profiles/kernels_NAME_stats.txt) when it is not the "
+                         "workload's own, e.g. for a run with another warm-up length")
     ap.add_argument("--sq-summary", metavar="COUNTER_CSV",
                     help="CPU only: write the SQ issue summary under profiles/ from a rocprofv3 "
                          "counter_collection.csv of the counters in SQ_COUNTERS")
@@ -416,8 +419,8 @@ def main(argv=None):
         write_sq_summary(args.sq_summary, label, args.pmc_commands, token_causal)
         return 0
     if args.stats_summary:
-        write_stats_summary(args.stats_summary, label, args.pmc_commands, token_causal, args.warmup,
-                            args.stats_bench_log)
+        write_stats_summary(args.stats_summary, args.stats_name or label, args.pmc_commands, token_causal,
+                            args.warmup, args.stats_bench_log)
         return 0
     if args.pmc_summary:
         write_traffic_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024,
