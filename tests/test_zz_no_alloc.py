@@ -49,9 +49,10 @@ def test_noalloc_equals_forward_on_consecutive_calls():
 
 def test_noalloc_ragged_shapes_and_repeat():
     """Ragged grids on both output-kernel variants (odd and even head counts),
-    each called twice in a row: identical results every time."""
+    and 34 x 60 frames (RoPE tables past 2,048 entries), each called twice in a
+    row: identical results every time."""
     import torch
-    for shape in [(5, 9, 13, 3, 128), (3, 5, 7, 4, 128), (2, 4, 4, 2, 64)]:
+    for shape in [(5, 9, 13, 3, 128), (3, 5, 7, 4, 128), (2, 4, 4, 2, 64), (2, 34, 60, 4, 128)]:
         T, H, W, heads, d = shape
         inp = make_inputs(T, H, W, heads, d, "bf16", seed=50)
         dev = to_device(inp)
