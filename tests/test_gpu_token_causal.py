@@ -268,3 +268,17 @@ def test_token_causal_large_frame_offset(dtype):
     ro, _, _ = _oracle_tc(inp, True, S0, z0, pos_offset=(t_off, 0, 0))
     plain, _, _ = _oracle_tc(inp, True, S0, z0)
     assert rel_err(plain, ro) > max(10 * rel_err(o, ro), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("include_self", [True, False])
+def test_token_causal_wide_frame(dtype, include_self):
+    """34 x 60 latent frames (1080p): the register pass 1 stages the wide RoPE
+    table (2,256 y and x entries) and the walk reads the global table."""
+    import gated_bidirectional_linear_amd as gla
+    code = gla.DTYPE_BF16 if dtype == "bf16" else gla.DTYPE_FP8_E4M3
+    p = gla.plan_describe("token_causal", (1, 34, 60), 2, 128, code)
+    assert (p["pass1_reg"], p["rope_lds1"], p["rope_lds2"]) == (1, 1, 0)
+    inp = make_inputs(1, 34, 60, 2, 128, dtype, seed=41)
+    S0, z0 = make_state(2, 128, seed=7)
+    _check(f"tc wide frame {dtype} incl={include_self}", inp, include_self, S0, z0)
