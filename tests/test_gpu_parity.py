@@ -116,6 +116,9 @@ SHAPES = [
     (2, 1, 1, 4, 128),     # 2 tokens
     (4, 16, 16, 2, 128),   # 1024 tokens: exact tiles
     (9, 15, 26, 2, 64),    # 3510 tokens
+    (2, 5, 9, 64, 128),    # 64 heads: 16 head quads, a chunk in 16-token tiles
+    (1, 3, 5, 128, 64),    # 128 heads at d = 64
+    (2, 4, 7, 40, 128),    # 40 heads: 10 head quads
 ]
 
 
