@@ -76,7 +76,10 @@ def relu(x: np.ndarray) -> np.ndarray:
 
 
 def sigmoid(x: np.ndarray) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+    # for x below about -709, exp(-x) overflows to inf and the value is 0, the
+    # function's limit; the overflow is expected and not reported
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
 
 
 def rope_axis_widths(d: int) -> tuple:
