@@ -33,12 +33,15 @@ def _graph_replays(fn, out, eager_ref, reps=3):
         _ = (eager_ref.float() * 2).sum().item()   # eager work between replays
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "e5m2"])
-def test_forward_graph_replay(dtype):
-    """Four heads at d = 128: the four-head output kernel (bf16 or fp8 rows)."""
+@pytest.mark.parametrize("dtype,grid", [("bf16", (4, 9, 10)), ("fp8", (4, 9, 10)), ("e5m2", (4, 9, 10)),
+                                        ("bf16", (2, 34, 60))], ids=lambda x: "x".join(map(str, x))
+                         if isinstance(x, tuple) else x)
+def test_forward_graph_replay(dtype, grid):
+    """Four heads at d = 128: the four-head output kernel (bf16 or fp8 rows);
+    34 x 60 frames run the wide-table pass 1."""
     torch = pytest.importorskip("torch")
     import gated_bidirectional_linear_amd as gla
-    inp = make_inputs(4, 9, 10, 4, 128, dtype, seed=51)
+    inp = make_inputs(*grid, 4, 128, dtype, seed=51)
     dev = to_device(inp)
     ref = gla.forward(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], dev["rms_w"], inp["grid"], eps=inp["eps"])
     torch.cuda.synchronize()
